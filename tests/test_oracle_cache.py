@@ -1,0 +1,119 @@
+"""Pins of the oracle's per-layer cross-loop cache (prefill, tail, flush, decode step).
+
+Facts pinned here come from the pages, not from the oracle: inactive tokens keep the
+previous loop's K/V (project page STEP 01); the most recent tokens stay exact BF16
+(PyPI Configuration; explainer section 3); the residual chain reconstructs each loop
+within that loop's own half quantization step; sparse loops that take every column
+reduce to dense attention.
+"""
+import numpy as np
+import pytest
+
+from quantized_kv_attention_amd import synth
+
+
+def test_body_tail_geometry(orc):
+    assert orc.body_len(0) == 0 and orc.body_len(63) == 0 and orc.body_len(127) == 0
+    assert orc.body_len(128) == 64 and orc.body_len(256) == 192
+    assert orc.body_len(32768) == 32704
+    for n in range(64, 600):
+        t = n - orc.body_len(n)
+        assert 64 <= t < 128 and orc.body_len(n) % 64 == 0
+
+
+@pytest.fixture(scope="module")
+def tiny_cache():
+    import oracle as orc
+    w = synth.WORKLOADS["tiny"]
+    K, V, act = synth.gen_layer(w)
+    cache = orc.OracleCache(w.B, w.H, w.d, w.R, cap=w.n + 80)
+    cache.prefill(K, V, act)
+    return w, K, V, act, cache
+
+
+def test_inactive_rows_reuse_previous_loop(tiny_cache):
+    w, K, V, act, c = tiny_cache
+    for r in range(1, w.R):
+        ina = ~act[r][0, :w.n]
+        assert ina.sum() > 0 or r < w.n_dense
+        for X in (c.Khat, c.Vhat):
+            a = X[r][0, 0, :w.n][ina]
+            b = X[r - 1][0, 0, :w.n][ina]
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_tail_rows_are_exact_bf16(tiny_cache, orc):
+    w, K, V, act, c = tiny_cache
+    nb = orc.body_len(w.n)
+    for r in range(w.R):
+        Kt = orc.bf16_bits_to_f32(K[r][0, 0, nb:w.n])
+        a = act[r][0, nb:w.n]
+        np.testing.assert_array_equal(c.Khat[r][0, 0, nb:w.n][a], Kt[a])
+
+
+def test_chain_error_is_per_loop(tiny_cache, orc):
+    # every active body row of every loop is within that loop's own half step of the
+    # exact input (the residual is taken against the reconstruction, so errors do not add up)
+    w, K, V, act, c = tiny_cache
+    nb = orc.body_len(w.n)
+    for r in range(w.R):
+        rec = c.planes[0][0][r]
+        valid = rec.pos >= 0
+        pos = rec.pos[valid]
+        assert np.all(act[r][0, pos]) and np.all(pos < nb)
+        if r < w.n_dense:
+            assert np.array_equal(pos, np.arange(nb))
+        ks = np.repeat(rec.ks, 64, axis=0)[valid]
+        vs = np.repeat(rec.vs, 64, axis=1)[valid]
+        errk = np.abs(c.Khat[r][0, 0, pos].astype(np.float64) - orc.bf16_bits_to_f32(K[r][0, 0, pos]))
+        errv = np.abs(c.Vhat[r][0, 0, pos].astype(np.float64) - orc.bf16_bits_to_f32(V[r][0, 0, pos]))
+        assert np.all(errk <= ks / 2 * (1 + 1e-5) + 1e-6)
+        assert np.all(errv <= vs / 2 * (1 + 1e-5) + 1e-6)
+
+
+def test_padding_layout(tiny_cache):
+    w, K, V, act, c = tiny_cache
+    rec = c.planes[0][0][2]  # loop 3: 25% of 256 tokens, body part only
+    n_valid = int((rec.pos >= 0).sum())
+    assert rec.pos.size % 64 == 0 and rec.pos.size - n_valid < 64
+    assert np.all(rec.kc[rec.pos < 0] == 0) and np.all(rec.vs[rec.pos < 0] == 0)
+    assert rec.ks.shape[0] == rec.pos.size // 64
+
+
+def test_flush_after_64_generated_tokens(orc):
+    w = synth.WORKLOADS["tiny"]
+    K, V, act = synth.gen_layer(w)
+    c = orc.OracleCache(w.B, w.H, w.d, w.R, cap=w.n + 80)
+    c.prefill(K, V, act)
+    nb0 = c.nb
+    slots0 = [c.planes[0][0][r].pos.size for r in range(w.R)]
+    for step in range(63):
+        k, v = synth.gen_new_token(w, step)
+        c.append(k, v)
+        assert c.nb == nb0
+    k, v = synth.gen_new_token(w, 63)
+    c.append(k, v)
+    assert c.nb == nb0 + 64 and c.n == w.n + 64 and c.n - c.nb == 64
+    for r in range(w.R):
+        rec = c.planes[0][0][r]
+        new = rec.pos[slots0[r]:]
+        exp = nb0 + np.nonzero(c.act[r][0, nb0:nb0 + 64])[0]
+        np.testing.assert_array_equal(new[new >= 0], exp)
+    # the newest token is stored exactly in every loop's tail
+    for r in range(w.R):
+        np.testing.assert_array_equal(c.Khat[r][0, 0, c.n - 1], orc.bf16_bits_to_f32(k[r][0, 0]))
+
+
+def test_step_all_columns_equals_dense(tiny_cache):
+    w, K, V, act, c = tiny_cache
+    q = synth.gen_queries(w, 0)
+    dense = c.step(q, n_dense=w.R, k=0)
+    sparse = c.step(q, n_dense=w.n_dense, k=w.n)
+    for r in range(w.R):
+        np.testing.assert_allclose(sparse[r]["o"], dense[r]["o"], rtol=0, atol=2e-6)
+    # with the default budget the sparse loops differ from dense but stay close
+    part = c.step(q, n_dense=w.n_dense, k=w.k_cols())
+    for r in range(w.n_dense, w.R):
+        assert part[r]["idx"][0][0].size == w.k_cols()
+        diff = np.abs(part[r]["o"] - dense[r]["o"]).max()
+        assert 0 < diff < 0.5
