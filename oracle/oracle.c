@@ -162,14 +162,15 @@ void orc_attend_dense(int n, int d, const float* q, double sm, const float* K, c
  * column's probability under the preceding distribution, p_j = exp(s_j - lse), and
  * their total mass m = sum p_j.  k >= n takes every column, k = 0 none.
  * ------------------------------------------------------------------------------- */
-static const float* g_sort_keys;
+typedef struct { float key; int32_t index; } orc_keyed;
+
 static int cmp_desc_then_index(const void* a, const void* b)
 {
-    int ia = *(const int32_t*)a, ib = *(const int32_t*)b;
-    float sa = g_sort_keys[ia], sb = g_sort_keys[ib];
-    if (sa > sb) return -1;
-    if (sa < sb) return 1;
-    return (ia < ib) ? -1 : (ia > ib);
+    const orc_keyed* x = (const orc_keyed*)a;
+    const orc_keyed* y = (const orc_keyed*)b;
+    if (x->key > y->key) return -1;
+    if (x->key < y->key) return 1;
+    return (x->index < y->index) ? -1 : (x->index > y->index);
 }
 static int cmp_index(const void* a, const void* b)
 {
@@ -182,15 +183,14 @@ int orc_select(int n, const float* scores, double lse, int k,
 {
     if (k > n) k = n;
     if (k < 0) k = 0;
-    int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
-    for (int j = 0; j < n; ++j) order[j] = j;
-    g_sort_keys = scores;
-    qsort(order, (size_t)n, sizeof(int32_t), cmp_desc_then_index);
-    qsort(order, (size_t)k, sizeof(int32_t), cmp_index);
+    orc_keyed* order = (orc_keyed*)malloc(sizeof(orc_keyed) * (size_t)(n > 0 ? n : 1));
+    for (int j = 0; j < n; ++j) { order[j].key = scores[j]; order[j].index = j; }
+    qsort(order, (size_t)n, sizeof(orc_keyed), cmp_desc_then_index);
+    for (int i = 0; i < k; ++i) idx[i] = order[i].index;
+    qsort(idx, (size_t)k, sizeof(int32_t), cmp_index);
     double m = 0.0;
     for (int i = 0; i < k; ++i) {
-        idx[i] = order[i];
-        p_sel[i] = exp((double)scores[order[i]] - lse);
+        p_sel[i] = exp((double)scores[idx[i]] - lse);
         m += p_sel[i];
     }
     *mass = m;

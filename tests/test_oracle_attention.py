@@ -188,3 +188,15 @@ def test_splice_unchanged_loop_is_identity(orc):
     o2, sc = orc.attend_sparse(q1, K1, V1, V1, idx, p64[idx], p64[idx].sum(), o1, lse1, s1)
     np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-14)
     np.testing.assert_allclose(sc, s1, rtol=0, atol=1e-12)
+
+
+def test_select_is_thread_safe(orc):
+    # the oracle is called from several threads at once (one per head)
+    from concurrent.futures import ThreadPoolExecutor
+    g = np.random.default_rng(11)
+    inputs = [g.standard_normal(5000).astype(np.float32) for _ in range(16)]
+    serial = [orc.select(s, 0.0, 500)[0] for s in inputs]
+    with ThreadPoolExecutor(8) as ex:
+        par = list(ex.map(lambda s: orc.select(s, 0.0, 500)[0], inputs * 4))
+    for i, idx in enumerate(par):
+        np.testing.assert_array_equal(idx, serial[i % 16])
