@@ -1,0 +1,197 @@
+/*
+ * qkv_attn.h - C ABI of libqkvattn.so: quantized cross-loop decode attention for
+ * looped Transformers on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (pages about "FlashLoop: Fast and Memory-Efficient Looped
+ * Transformers via Lazy Updates"):
+ *   - project page, The Method, STEP 03; flozi.net explainer section 3: loop 1's K/V
+ *     are stored as an INT4 base and every later loop as the INT4 residual against the
+ *     previous loop's reconstruction, group size 64, asymmetric scale/zero, keys grouped
+ *     per channel over 64 tokens, values per token over 64 channels, the most recent
+ *     tokens kept in BF16;
+ *   - project page STEP 01: residual rows exist for active tokens only, inactive tokens
+ *     reuse the previous loop's K/V;
+ *   - project page STEP 02; explainer section 3: sparse late loops attend to the top-K
+ *     key columns of the preceding loop's distribution, cache those columns' probability
+ *     mass m under that full distribution, and correct the preceding loop's output for
+ *     those columns only (a rank-K correction that keeps mass m);
+ *   - PyPI page, Configuration: 4 loops, dense loops 1-2, 10% key budget, 4-bit, group
+ *     64, 64-token BF16 tail, head dimension 128, batch one (batch > 1 is supported here).
+ *
+ * Conventions for every entry point
+ *   - Pointers documented as "device" are HIP device memory owned by the caller; the
+ *     library never allocates, frees or retains them and keeps no state between calls.
+ *   - Work is queued on `stream` (a hipStream_t; NULL = the default stream) and is
+ *     asynchronous: results are valid once the stream has reached that point.
+ *   - Arguments are checked on the host before anything is queued; on error nothing is
+ *     queued and a negative status is returned (see qkv_strerror).  Device-side contents
+ *     (active lists, index lists) are trusted: they must satisfy the stated contracts.
+ *   - Device buffers must be 16-byte aligned.  bf16 values are passed as uint16_t bits.
+ *   - Calls that share a cache or a workspace must not overlap in time (same stream or
+ *     explicit ordering).
+ */
+#ifndef QKV_ATTN_H
+#define QKV_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QKV_MAX_LOOPS 32
+#define QKV_GROUP 64
+#define QKV_TAIL_SLOTS 128
+
+enum {
+    QKV_OK = 0,
+    QKV_EINVAL = -1,        /* bad argument (null pointer, size out of range, misalignment) */
+    QKV_EUNSUPPORTED = -2,  /* head_dim not 64/128, loop count above QKV_MAX_LOOPS, ...     */
+    QKV_ECAPACITY = -3,     /* positions or rows beyond the buffers the cache describes     */
+    QKV_ELAUNCH = -4,       /* a HIP launch failed                                           */
+    QKV_EWORKSPACE = -5     /* workspace missing or smaller than qkv_workspace_bytes()      */
+};
+
+/*
+ * One loop's stored plane (loop p = index + 1).  Layout of `data`, device memory:
+ *   [batch][heads][n_blocks][block], one block = 64 consecutive storage slots, with
+ *   block = K codes [64][d/2] | V codes [64][d/2] | K s[d], K z[d] (fp32)
+ *           | V meta [64][d/64] of (s, z) (fp32)                   -> qkv_block_bytes(d)
+ *   A code byte holds channel 2i in its low nibble and channel 2i+1 in its high nibble.
+ *   Key group = one block (64 consecutive slots) per channel; value group = one slot
+ *   over 64 consecutive channels.  Dequantised value = fmaf(code, s, z).
+ * A dense plane stores every body position at slot == position.  A sparse plane stores
+ * the active positions in ascending order; each encode call starts on a new block and
+ * pads its last block (padding slots: codes 0, value meta 0, rowpos -1).  Sparse planes
+ * need the three maps below (device int32, caller-allocated; rowstart[b][0] must be 0
+ * before the first encode of the plane; rowmap/rowpos need no initialisation):
+ *   rowmap   [batch][cap_ctx]          position -> slot, -1 if not stored
+ *   rowpos   [batch][n_blocks * 64]    slot -> position, -1 for padding
+ *   rowstart [batch][cap_ctx/64 + 1]   first slot holding a position >= 64*i
+ * Loop 1 (the base) must be dense.
+ */
+typedef struct qkv_plane {
+    void* data;
+    int32_t n_blocks;
+    int32_t dense;
+    int32_t* rowmap;
+    int32_t* rowpos;
+    int32_t* rowstart;
+} qkv_plane;
+
+/*
+ * One layer's cross-loop cache.  Column (position) geometry, same for every sequence:
+ *   body = [0, n_body) with n_body = 64 * floor((n_ctx - 64) / 64) (0 if n_ctx < 64),
+ *   tail = [n_body, n_ctx), so 64 <= n_ctx - n_body < 128 once n_ctx >= 64.
+ * Body positions live in the planes; tail positions in the per-loop BF16 tails
+ *   tail_k[p], tail_v[p]: device bf16 [batch][heads][128][head_dim], position t at slot
+ *   t % 128, holding loop p+1's value (an inactive token holds loop p's value).
+ * The caller advances n_ctx; when the body boundary moves, the 64 positions that leave
+ * the tail must first be encoded into every loop's plane (kv_encode_loop with
+ * k_src == NULL, loops in order).
+ */
+typedef struct qkv_cache {
+    int32_t batch, heads, head_dim, n_loops;
+    int32_t cap_ctx;   /* capacity in positions, a multiple of 64 */
+    int32_t n_ctx;     /* cached positions (attention columns) of every sequence */
+    qkv_plane plane[QKV_MAX_LOOPS];
+    uint16_t* tail_k[QKV_MAX_LOOPS];
+    uint16_t* tail_v[QKV_MAX_LOOPS];
+} qkv_cache;
+
+/* Human-readable text of a status code (static storage). */
+const char* qkv_strerror(int status);
+
+/* Bytes of one 64-slot block for head_dim d (d = 128: 10240; d = 64: 5120), 0 if unsupported. */
+size_t qkv_block_bytes(int head_dim);
+
+/* Body length for a context of n positions (see qkv_cache). */
+int qkv_body_len(int n_ctx);
+
+/*
+ * Workspace bytes that attn_decode_dense, attn_decode_sparse and select_columns need for
+ * caches of this shape with up to max_ctx positions and up to max_k selected columns.
+ * The workspace is device memory owned by the caller; it must be zero-filled once
+ * before its first use and is left zero-filled by every call.
+ */
+size_t qkv_workspace_bytes(int batch, int heads, int head_dim, int max_ctx, int max_k);
+
+/*
+ * kv_encode_loop - residual-quantize encode of one loop for positions [pos0, pos0+n_pos)
+ * [project page STEP 03; explainer section 3].
+ *   loop     1..n_loops; loops must be encoded in order for a position range, because
+ *            loop r stores X^(r) - Xhat^(r-1) and rebuilds Xhat^(r-1) from planes 1..r-1.
+ *   pos0     multiple of 64; n_pos a positive multiple of 64; pos0 + n_pos <= cap_ctx.
+ *   act_pos  device int32 [batch][ld_act]: ascending active positions of each sequence,
+ *            all in [pos0, pos0+n_pos); n_act device int32 [batch] their counts.
+ *            Both must be NULL for a dense plane (every position active).
+ *   k_src, v_src  device bf16 [batch][heads][ld_src][head_dim]: row i = the i-th active
+ *            position's K^(loop) / V^(loop) (post-RoPE keys).  If both are NULL the rows
+ *            are read from tail_k/tail_v[loop-1] (flushing tail positions into the body).
+ * Writes the plane's blocks for these slots (and, for a sparse plane, its maps).
+ * Codes, scales and zeros follow the quantizer exactly: s = (max-min)/15, z = min (fp32,
+ * -0 stored as +0), code = clamp(rint((x - z)/s), 0, 15), code 0 when s == 0.
+ */
+int kv_encode_loop(const qkv_cache* cache, int loop, int pos0, int n_pos,
+                   const int32_t* act_pos, const int32_t* n_act, int ld_act,
+                   const uint16_t* k_src, const uint16_t* v_src, int ld_src, void* stream);
+
+/*
+ * kv_append_tail - writes n_rows consecutive positions pos0.. of loop `loop` into the BF16
+ * tail ring [PyPI Configuration: 64-token BF16 residual tail].
+ *   k, v: device bf16 [batch][heads][n_rows][head_dim].  1 <= n_rows <= 128.
+ */
+int kv_append_tail(const qkv_cache* cache, int loop, int pos0, int n_rows,
+                   const uint16_t* k, const uint16_t* v, void* stream);
+
+/*
+ * attn_decode_dense - dense decode attention of loop `loop` over all n_ctx columns
+ * [explainer section 1: decode reads every cached column; textbook softmax attention].
+ *   Keys/values of column j are the loop's reconstruction: base plus every residual
+ *   plane p <= loop in which j is stored (BF16 tail values for tail columns).
+ *   q        device bf16 [batch][heads][head_dim]; sm_scale multiplies the logits.
+ *   o        device bf16 [batch][heads][head_dim] (may be NULL); o_f32 device fp32 same shape.
+ *   scores   device fp32 [batch][heads][ld_scores]: raw logits s_j, j < n_ctx.
+ *   lse      device fp32 [batch][heads]: log sum_j exp(s_j).
+ */
+int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, float sm_scale,
+                      uint16_t* o, float* o_f32, float* scores, int ld_scores, float* lse,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * select_columns - top-k columns of each (sequence, head) under the distribution
+ * exp(scores - lse) [project page STEP 02; PyPI Configuration: 10% key retention].
+ *   Order: fp32 score descending, ties to the lower index (+0 and -0 are equal).
+ *   0 <= k <= n (k == n takes every column); n <= ld_scores.  Writes k entries per
+ *   (sequence, head):
+ *   idx    device int32 [batch][heads][k]: selected columns, ascending.
+ *   p_sel  device fp32 [batch][heads][k]: exp(scores[idx] - lse).
+ *   mass   device fp32 [batch][heads]: sum of p_sel (cached mass m).
+ */
+int select_columns(const float* scores, int ld_scores, const float* lse, int batch, int heads,
+                   int n, int k, int32_t* idx, float* p_sel, float* mass,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * attn_decode_sparse - sparse loop `loop` (>= 2): recompute only the selected columns and
+ * correct the previous loop's output [project page STEP 02; explainer section 3]:
+ *   s_j = sm_scale * q . khat^(loop)_j for j in S, alpha = softmax over S of s,
+ *   o = o_prev + sum_{j in S} (m * alpha_j * vhat^(loop)_j - p_sel_j * vhat^(loop-1)_j),
+ *   scores[j] <- lse + log(m) + s_j - log sum_{i in S} exp(s_i)   for j in S (in place),
+ * so the selected columns keep their cached mass m.  Other scores and lse are unchanged.
+ *   idx, p_sel, mass as written by select_columns; k entries per (sequence, head),
+ *   0 <= k <= n_ctx (k == 0: o = o_prev).
+ *   o_prev   device fp32 [batch][heads][head_dim]: previous loop's output (full precision).
+ *   lse      device fp32 [batch][heads]: the lse the selection used.
+ */
+int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, float sm_scale,
+                       const int32_t* idx, const float* p_sel, const float* mass, int k,
+                       const float* o_prev, const float* lse, float* scores, int ld_scores,
+                       uint16_t* o, float* o_f32, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKV_ATTN_H */

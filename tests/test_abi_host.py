@@ -1,0 +1,103 @@
+"""The C ABI library loads without a GPU, exports every declared entry point, and rejects
+bad arguments on the host before queueing any work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_kv_attention_amd as qkv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qkv_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "sizeof")))
+
+
+def test_exports_every_declared_symbol():
+    L = qkv.lib()
+    names = declared_functions()
+    assert set(names) == set(qkv.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_sizes():
+    assert qkv.block_bytes(128) == 10240 and qkv.block_bytes(64) == 5120 and qkv.block_bytes(96) == 0
+    assert qkv.body_len(0) == 0 and qkv.body_len(127) == 0 and qkv.body_len(256) == 192
+    assert qkv.body_len(32768) == 32704
+    assert qkv.workspace_bytes(1, 16, 128, 32768, 3277) > 16 * (512 + 1) * 130 * 4 * 0
+    assert qkv.workspace_bytes(1, 16, 96, 32768, 3277) == 0
+    assert qkv.strerror(qkv.QKV_EINVAL) == "invalid argument"
+
+
+def _desc(**kw):
+    d = qkv.QkvCache()
+    d.batch, d.heads, d.head_dim, d.n_loops, d.cap_ctx, d.n_ctx = 1, 1, 128, 2, 256, 256
+    for r in range(2):
+        d.plane[r].data = 4096 * (r + 1)
+        d.plane[r].n_blocks = 4
+        d.plane[r].dense = 1
+        d.tail_k[r] = 65536 * (r + 1)
+        d.tail_v[r] = 65536 * (r + 3)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+class _C:
+    def __init__(self, desc):
+        self.desc = desc
+
+
+@pytest.mark.parametrize("mut,expect", [
+    (dict(head_dim=96), qkv.QKV_EUNSUPPORTED),
+    (dict(n_loops=33), qkv.QKV_EUNSUPPORTED),
+    (dict(cap_ctx=100), qkv.QKV_EINVAL),
+    (dict(n_ctx=300), qkv.QKV_ECAPACITY),
+    (dict(batch=0), qkv.QKV_EINVAL),
+])
+def test_descriptor_validation(mut, expect):
+    L = qkv.lib()
+    d = _desc(**mut)
+    vp = ctypes.c_void_p
+    st = L.attn_decode_dense(ctypes.byref(d), 1, vp(16), 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None)
+    assert st == expect
+
+
+def test_argument_validation():
+    L = qkv.lib()
+    vp = ctypes.c_void_p
+    d = _desc()
+    # loop out of range, null query, misaligned pointer, short workspace
+    assert L.attn_decode_dense(ctypes.byref(d), 3, vp(16), 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(18), 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), 1.0, None, vp(16), vp(16), 100, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 16, None) == qkv.QKV_EWORKSPACE
+    # sparse loop 1 is not allowed; k beyond the context is not allowed
+    assert L.attn_decode_sparse(ctypes.byref(d), 1, vp(16), 1.0, vp(16), vp(16), vp(16), 4, vp(16), vp(16), vp(16), 256, None, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_sparse(ctypes.byref(d), 2, vp(16), 1.0, vp(16), vp(16), vp(16), 300, vp(16), vp(16), vp(16), 256, None, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    # encode: unaligned range, dense plane with an active list, beyond capacity, tail rows not in the tail
+    assert L.kv_encode_loop(ctypes.byref(d), 1, 32, 64, None, None, 0, vp(16), vp(16), 64, None) == qkv.QKV_EINVAL
+    assert L.kv_encode_loop(ctypes.byref(d), 1, 0, 64, vp(16), vp(16), 64, vp(16), vp(16), 64, None) == qkv.QKV_EINVAL
+    assert L.kv_encode_loop(ctypes.byref(d), 1, 256, 64, None, None, 0, vp(16), vp(16), 64, None) == qkv.QKV_ECAPACITY
+    assert L.kv_encode_loop(ctypes.byref(d), 1, 0, 64, None, None, 0, None, None, 0, None) == qkv.QKV_EINVAL
+    # a sparse base plane is rejected
+    d2 = _desc()
+    d2.plane[0].dense = 0
+    assert L.kv_encode_loop(ctypes.byref(d2), 1, 0, 64, None, None, 0, vp(16), vp(16), 64, None) == qkv.QKV_EINVAL
+    # select: k above n
+    assert L.select_columns(vp(16), 256, vp(16), 1, 1, 256, 257, vp(16), vp(16), vp(16), None, 0, None) == qkv.QKV_EINVAL
+    assert L.kv_append_tail(ctypes.byref(d), 1, 0, 129, vp(16), vp(16), None) == qkv.QKV_EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(qkv, "_lib", None)
+    monkeypatch.setattr(qkv, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError):
+        qkv.lib()

@@ -1,0 +1,116 @@
+"""GPU parity: the HIP path against the oracle on the same seeded inputs.
+
+Bit-exact: INT4 codes, fp32 scales/zeros, storage maps and the top-k index sets (the
+selection compared on identical fp32 scores).  Tolerance: bf16 outputs within rel-L2
+2e-3 and max-abs 1e-2 of the oracle rounded to bf16.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import Pair, assert_out, check_step, compare_planes, say, to_dev_bf16
+from quantized_kv_attention_amd import cache as qcache
+from quantized_kv_attention_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def test_tiny_codes_and_step():
+    w = W["tiny"]
+    say(f"tiny: {w}")
+    p = Pair(w, extra=80)
+    compare_planes(p.gpu, p.orc, [0], [0])
+    check_step(p, p.queries(0), w.n_dense, w.k_cols(p.n), "tiny")
+
+
+def test_tiny_decode_with_flush():
+    w = W["tiny"]
+    p = Pair(w, extra=80)
+    for step in range(64):
+        p.append(step)
+        if step in (0, 62):
+            check_step(p, p.queries(step + 1), w.n_dense, w.k_cols(p.gpu.n_ctx), f"tiny step {step}")
+    assert p.gpu.n_ctx == w.n + 64 and p.orc.nb == w.n - 64 + 64
+    compare_planes(p.gpu, p.orc, [0], [0])
+    check_step(p, p.queries(99), w.n_dense, w.k_cols(p.gpu.n_ctx), "tiny after flush")
+
+
+@pytest.mark.parametrize("n", [1, 37, 64, 100, 128, 191])
+def test_short_contexts(n):
+    w = W["tiny"]
+    p = Pair(w, n=n, extra=8)
+    compare_planes(p.gpu, p.orc, [0], [0])
+    check_step(p, p.queries(1), w.n_dense, w.k_cols(n), f"n={n}")
+
+
+def test_ragged_d128_multihead():
+    # 16x128 shape at a ragged length: body 896 + tail 104, several splits and chunks
+    w = dataclasses.replace(W["ctx4k"], H=3)
+    p = Pair(w, n=1000, extra=70)
+    compare_planes(p.gpu, p.orc, range(3), range(3))
+    check_step(p, p.queries(0), w.n_dense, w.k_cols(1000), "n=1000 d=128")
+    for step in range(25):
+        p.append(step)
+    compare_planes(p.gpu, p.orc, range(3), range(3))
+    check_step(p, p.queries(30), w.n_dense, w.k_cols(p.gpu.n_ctx), "n=1025 d=128 after flush")
+
+
+def test_batch_with_different_masks():
+    w = dataclasses.replace(W["batch8"], B=3, H=2)
+    p = Pair(w, n=700, extra=8)
+    a = p.act[2]
+    assert not np.array_equal(a[0], a[1])
+    compare_planes(p.gpu, p.orc, range(2), range(2))
+    check_step(p, p.queries(0), w.n_dense, w.k_cols(700), "batch 3")
+
+
+def test_deep_recurrence_32_loops():
+    w = dataclasses.replace(W["deep32"], H=2)
+    p = Pair(w, n=900, extra=8)
+    compare_planes(p.gpu, p.orc, range(2), range(2))
+    check_step(p, p.queries(0), w.n_dense, w.k_cols(900), "R=32")
+
+
+def test_all_columns_is_dense_on_gpu():
+    w = dataclasses.replace(W["ctx4k"], H=2)
+    p = Pair(w, n=777, extra=8)
+    q = p.queries(3)
+    dense = p.run_gpu_loopwise(q, w.R, 0)
+    full = p.run_gpu_loopwise(q, w.n_dense, 777)
+    for r in range(w.R):
+        rel = np.linalg.norm(full[r]["o_f32"] - dense[r]["o_f32"]) / np.linalg.norm(dense[r]["o_f32"])
+        say(f"  k=n loop {r + 1}: rel-L2 vs dense {rel:.2e}")
+        assert rel < 1e-5
+
+
+def test_no_columns_keeps_previous_output():
+    w = W["tiny"]
+    p = Pair(w, extra=8)
+    s = p.run_gpu_loopwise(p.queries(2), w.n_dense, 0)
+    for r in range(w.n_dense, w.R):
+        assert np.array_equal(s[r]["o_f32"], s[r - 1]["o_f32"])
+
+
+def test_special_values_codes():
+    # constant channel groups, constant rows, a tiny-magnitude (denormal-range) group, -0
+    w = dataclasses.replace(W["tiny"], rho=[1, 1, 1, 1])
+    p = Pair(w, extra=8)
+    import oracle as orc
+    K, V, act = synth.gen_layer(w)
+    K = [k.copy() for k in K]
+    V = [v.copy() for v in V]
+    K[0][0, 0, :64, 5] = synth.bf16_round_bits(np.full(64, 1.5, np.float32))
+    V[0][0, 0, 3, :64] = synth.bf16_round_bits(np.full(64, -2.25, np.float32))
+    K[0][0, 0, 64:128, 7] = synth.bf16_round_bits(np.linspace(-1e-38, 1e-38, 64).astype(np.float32))
+    K[0][0, 0, 128:192, 9] = np.uint16(0x8000)
+    cap = 256 + 64
+    g = qcache.LayerCache(1, 1, w.d, w.R, cap, dense=[True] * 4)
+    g.prefill([to_dev_bf16(k) for k in K], [to_dev_bf16(v) for v in V], act)
+    o = orc.OracleCache(1, 1, w.d, w.R, cap)
+    o.prefill(K, V, act)
+    torch.cuda.synchronize()
+    compare_planes(g, o, [0], [0])
