@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Decode-attention bench: quantized cross-loop KV cache, 32K context, 4 loops, one MI355X.
+
+One step = one decode step of every rotated layer, run loop-major as a looped model does
+(loop r over all layers before loop r+1): the new token's K/V appended to every loop's
+BF16 tail (plus, once every 64 steps, the 64-row tail flush into every loop's plane),
+dense attention in loops 1-2, top-k selection and the sparse splice in loops 3-4.
+Eight distinct layer caches (about 200 MB each) rotate so that no loop finds its planes
+in the 256 MB last-level cache.  Steps are replayed from two captured HIP graphs (with and
+without the flush); the context stays at n+1 columns.
+
+Prints one JSON line.  `value` is microseconds per decode step of one layer (lower is
+better); `roofline` reports the dominant kernel (the loop-2 dense reader, which streams
+the base and the loop-2 residual plane) against the 8 TB/s HBM peak; `cpu_baseline` times
+the fp64 oracle on a sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--workload", default="ctx32k")
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-steps", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=4, help="timed launches per layer of the dominant kernel")
+    ap.add_argument("--profile-dense", action="store_true",
+                    help="only launch the loop-2 dense reader (for counter runs)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by head with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_kv_attention_amd as qkv
+    from quantized_kv_attention_amd import bytes_model as bm
+    from quantized_kv_attention_amd import cache as qcache
+    from quantized_kv_attention_amd import synth
+
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    L = args.layers
+    n = w.n
+    n_step = n + 1                       # context of the step: prompt + the new token
+    k = w.k_cols(n_step)
+    cap = int(math.ceil((n + 128) / 64) * 64)
+    nb = qkv.body_len(n_step)
+    dense = [w.rho[r] >= 1.0 for r in range(w.R)]
+
+    def dev(u16):
+        return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+    t_setup = time.time()
+    layers = []
+    for l in range(L):
+        K, V, act = synth.gen_layer_torch(w, l)
+        c = qcache.LayerCache(w.B, w.H, w.d, w.R, cap, dense=dense)
+        c.prefill(K, V, act)
+        del K, V
+        bufs = qcache.DecodeBuffers(c, max_k=k)
+        qs = [dev(x) for x in synth.gen_queries(w, 1000 + l)]
+        kn, vn = synth.gen_new_token(w, 1000 + l)
+        kn = [dev(x).view(w.B, w.H, 1, w.d) for x in kn]
+        vn = [dev(x).view(w.B, w.H, 1, w.d) for x in vn]
+        c.act[:, :, n] = True
+        flush = []
+        for r in range(w.R):
+            if dense[r]:
+                flush.append(None)
+            else:
+                ap, na = c._active_lists(r, nb, nb + 64)
+                flush.append((torch.from_numpy(ap).cuda(), torch.from_numpy(na).cuda()))
+        c.n_ctx = n_step
+        layers.append(dict(c=c, b=bufs, q=qs, kn=kn, vn=vn, flush=flush, act=act))
+        torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    setup_s = time.time() - t_setup
+    print(f"[bench] {L} layer caches of {layers[0]['c'].nbytes() / 1e6:.1f} MB ready in {setup_s:.1f}s "
+          f"(n={n_step}, k={k})", file=sys.stderr, flush=True)
+
+    def step(with_flush):
+        for ly in layers:
+            c = ly["c"]
+            if with_flush:
+                for r in range(w.R):
+                    f = ly["flush"][r]
+                    if f is None:
+                        qkv.kv_encode_loop(c, r + 1, nb, 64)
+                    else:
+                        qkv.kv_encode_loop(c, r + 1, nb, 64, f[0], f[1])
+            for r in range(w.R):
+                qkv.kv_append_tail(c, r + 1, n, ly["kn"][r], ly["vn"][r])
+        for loop in range(1, w.R + 1):
+            for ly in layers:
+                qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k)
+
+    def dense2():
+        for ly in layers:
+            qcache.decode_loop(ly["c"], ly["b"], 2, ly["q"][1], w.n_dense, k)
+
+    if args.profile_dense:
+        for _ in range(args.warmup + args.steps):
+            dense2()
+        torch.cuda.synchronize()
+        print("[bench] dense-reader profiling run done", file=sys.stderr, flush=True)
+        return
+
+    # eager warm-up, then capture the two step variants
+    step(True)
+    step(False)
+    torch.cuda.synchronize()
+    g_plain, g_flush = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_plain):
+        step(False)
+    with torch.cuda.graph(g_flush):
+        step(True)
+    for _ in range(args.warmup):
+        g_plain.replay()
+    torch.cuda.synchronize()
+    # graph replays give the eager result
+    ref_o = layers[0]["b"].o_f32.clone()
+    step(False)
+    torch.cuda.synchronize()
+    eager_o = layers[0]["b"].o_f32.clone()
+    g_plain.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(eager_o, layers[0]["b"].o_f32) and torch.equal(ref_o, eager_o), "graph replay differs"
+
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for i in range(K):
+        (g_flush if (i % 64) == 63 else g_plain).replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = e0.elapsed_time(e1)
+    n_flush = sum(1 for i in range(K) if (i % 64) == 63)
+    us_step_layer = total_ms * 1000.0 / (K * L)
+    print(f"[bench] {K} steps x {L} layers: {total_ms:.2f} ms (wall {wall * 1e3:.2f} ms), "
+          f"{us_step_layer:.2f} us per layer-step", file=sys.stderr, flush=True)
+
+    # ---- algorithmic bytes of one layer-step (from the actual masks and selections) ----
+    c0, b0, act0 = layers[0]["c"], layers[0]["b"], layers[0]["act"]
+    T = n_step - nb
+    B, H, d = w.B, w.H, w.d
+    rows = []
+    slots = []
+    for r in range(w.R):
+        per_b = []
+        sl = []
+        for b in range(B):
+            if dense[r]:
+                per_b.append(nb)
+                sl.append(np.arange(nb))
+            else:
+                a = act0[r][b, :nb]
+                s = np.full(nb, -1, np.int64)
+                s[a] = np.arange(int(a.sum()))
+                per_b.append(int(a.sum()))
+                sl.append(s)
+        rows.append(per_b)
+        slots.append(sl)
+    step_bytes = 0
+    loop_bytes = []
+    for r in range(w.R):
+        lb = 0
+        if r < w.n_dense:
+            for b in range(B):
+                lb += H * bm.dense_loop_bytes([rows[p][b] for p in range(r + 1)], T, n_step, d)
+        else:
+            # the selection loop r made in the last replay
+            idx_all = b0.selection(r + 1, k)[0].cpu().numpy()
+            lb += B * H * bm.select_bytes(n_step, k)
+            for b in range(B):
+                for h in range(H):
+                    lb += bm.sparse_loop_bytes(idx_all[b, h], [slots[p][b] for p in range(r + 1)], nb, d)
+        loop_bytes.append(lb)
+        step_bytes += lb
+    append_bytes = w.R * B * H * d * 2 * 2 * 2               # read new K/V, write the tail rows
+    # flush of the 64 oldest tail rows: BF16 rows in, the loop's plane rows out, and the
+    # rows' chain through planes 1..r-1 re-read to form the residual
+    flush_bytes = 0
+    for r in range(w.R):
+        for b in range(B):
+            stored = 64 if dense[r] else int(act0[r][b, nb:nb + 64].sum())
+            flush_bytes += H * (stored * d * 2 * 2 + bm.plane_bytes(stored, d) * (r + 1))
+    step_bytes += append_bytes + flush_bytes * n_flush / K
+    gbps_step = step_bytes / (us_step_layer * 1e-6) / 1e9
+
+    # ---- dominant kernel: the loop-2 dense reader, timed launch by launch on its stream ----
+    dense2_bytes = loop_bytes[1]
+    s = torch.cuda.current_stream()
+    evs = []
+    for rep in range(args.kernel_reps):
+        for ly in layers:
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(s)
+            qkv.attn_decode_dense(ly["c"], 2, ly["q"][1], 1.0, ly["b"].o[1], ly["b"].o_f32[1], ly["b"].scores,
+                                  ly["b"].lse, ly["b"].ws, s)
+            a1.record(s)
+            evs.append((a0, a1))
+    torch.cuda.synchronize()
+    durs = sorted(a0.elapsed_time(a1) * 1000.0 for a0, a1 in evs)
+    dense2_us = float(np.mean(durs))
+    dense2_med = durs[len(durs) // 2]
+    achieved = dense2_bytes / (dense2_us * 1e-6) / 1e9
+    print(f"[bench] loop-2 dense reader: {dense2_bytes / 1e6:.1f} MB/launch, mean {dense2_us:.2f} us "
+          f"(median {dense2_med:.2f}) -> {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "dense_loop2_ctx32k_traffic.json")
+    if os.path.exists(tfile):
+        try:
+            t = json.load(open(tfile))
+            if t.get("kernel_source_hash") == _dense_source_hash():
+                traffic = t.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_heads, args.cpu_steps)
+
+    out = {
+        "metric": "decode-attn us/step & achieved HBM GB/s (% peak), 32K ctx, 4 loops, 1 GPU",
+        "value": round(us_step_layer, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: batch {B}, {H} heads x {d}, context {n_step}, {w.R} loops, "
+                               f"token retention {w.rho}, {int(w.k_frac * 100)}% key columns in loops "
+                               f"{w.n_dense + 1}-{w.R}, INT4 g64 + fp32 scale/zero, 64-token BF16 tail",
+                   "layers_rotated": L, "k_columns": k, "step": "append + amortised 64-row flush + R-loop attention",
+                   "value_is": "microseconds per decode step of one layer"},
+        "hbm_GBps_step": round(gbps_step, 1),
+        "pct_peak_step": round(100 * gbps_step / HBM_PEAK_GBPS, 2),
+        "bytes_per_layer_step": int(step_bytes),
+        "bytes_per_loop": [int(x) for x in loop_bytes],
+        "roofline": {"bound": "hbm", "kernel": "dense_split_kernel<128> (loop 2: base + loop-2 residual plane)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "bytes_per_launch": int(dense2_bytes), "mean_launch_us": round(dense2_us, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _dense_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("dense.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "quantized_kv_attention_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(w, heads, steps):
+    """The fp64 oracle on `heads` heads of the same workload, one decode step (all loops)
+    from the encoded cache per query, scaled to all heads of one layer."""
+    import numpy as np
+
+    import oracle as orc
+    from quantized_kv_attention_amd import synth
+
+    hs = list(range(min(heads, w.H)))
+    K, V, act = synth.gen_layer(w, heads=hs)
+    oc = orc.OracleCache(w.B, len(hs), w.d, w.R, w.n + 128)
+    oc.prefill(K, V, act)
+    del K, V
+    kn, vn = synth.gen_new_token(w, 1000, heads=hs)
+    oc.append(kn, vn)
+    k = w.k_cols(oc.n)
+    threads = min(len(hs) * w.B, os.cpu_count() or 1)
+    qs = [synth.gen_queries(w, 2000 + s, heads=hs) for s in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        oc.step(qs[s], w.n_dense, k, threads=threads)
+    dt = time.perf_counter() - t0
+    per_step_us = dt / steps * 1e6 * (w.H / len(hs))
+    return {"value": round(per_step_us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"{len(hs)} of {w.H} heads x {steps} decode steps (all {w.R} loops, context {oc.n}), "
+                      f"{dt:.1f} s wall, scaled to {w.H} heads"}
+
+
+if __name__ == "__main__":
+    main()

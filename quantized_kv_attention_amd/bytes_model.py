@@ -1,0 +1,74 @@
+"""Algorithmic byte counts of the decode path and of the stored cache.
+
+Bytes are counted from what each step must touch at least once: INT4 codes (half a byte
+per element), fp32 scale/zero pairs (8 bytes per group), BF16 tail rows, query, scores
+and outputs.  Sparse loops are counted from the actual selection: the codes and value
+metadata of every selected column in every plane that stores it, and the key metadata
+of every distinct (plane, key group) the selection touches.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 64
+
+
+def plane_bytes(rows: int, d: int) -> int:
+    """One stored plane of `rows` slots: K+V codes, K metadata per 64-slot group, V metadata per slot."""
+    groups = (rows + GROUP - 1) // GROUP
+    return rows * d + groups * d * 8 + rows * (d // GROUP) * 8
+
+
+def dense_loop_bytes(rows_per_plane, tail_rows: int, n: int, d: int) -> int:
+    """Dense loop r for one (sequence, head): planes 1..r, the loop's BF16 tail, q, scores, o."""
+    b = sum(plane_bytes(r, d) for r in rows_per_plane)
+    b += tail_rows * d * 2 * 2          # BF16 K and V rows of the tail
+    b += d * 2                          # query
+    b += n * 4                          # raw scores written for the next selection
+    b += d * (2 + 4) + 4                # o (bf16 + fp32) and lse
+    return b
+
+
+def select_bytes(n: int, k: int) -> int:
+    return n * 4 + 4 + k * 8 + 4        # scores + lse in; idx + p_sel + mass out
+
+
+def sparse_loop_bytes(idx: np.ndarray, slots_per_plane, n_body: int, d: int) -> int:
+    """Sparse loop r for one (sequence, head).
+
+    idx: selected columns (ascending).  slots_per_plane[p]: int array over body positions
+    giving the slot of each position in plane p (-1 if not stored), for p = 1..r.
+    """
+    idx = np.asarray(idx)
+    body = idx[idx < n_body]
+    ntail = int((idx >= n_body).sum())
+    b = 0
+    for slots in slots_per_plane:
+        s = slots[body]
+        s = s[s >= 0]
+        b += s.size * (d + (d // GROUP) * 8)        # K+V codes + V metadata of each stored column
+        b += np.unique(s // GROUP).size * d * 8      # K metadata of each touched key group
+    b += ntail * d * 2 * 3                          # tail K^(r), V^(r), V^(r-1)
+    b += idx.size * (4 + 4)                         # idx, p_sel
+    b += idx.size * (4 + 4)                         # score written, then shifted in place
+    b += d * 2 + d * 4 + d * (2 + 4) + 4 + 4       # q, o_prev, o (bf16 + fp32), mass, lse
+    return b
+
+
+def cache_payload_bytes(n: int, d: int, heads: int, layers: int, retained, tail_tokens: int = 64,
+                        metadata: bool = True) -> dict:
+    """Stored bytes of a cross-loop cache at context n.
+
+    retained[r]: fraction of tokens stored by loop r+1.  Without metadata, INT4 is one
+    quarter of BF16; the most recent `tail_tokens` tokens of every loop stay BF16.
+    """
+    bf16_per_loop = 2 * 2 * heads * d * layers * n               # K and V, 2 bytes each
+    packed = sum(bf16_per_loop / 4 * r for r in retained)
+    if metadata:
+        for r in retained:
+            rows = r * n
+            packed += (np.ceil(rows / GROUP) * d * 8 + rows * (d // GROUP) * 8) * 2 * heads * layers / 2
+    tail_extra = 2 * 2 * heads * d * layers * tail_tokens * len(retained) * (1 - 1 / 4)
+    baseline = bf16_per_loop * len(retained)
+    return dict(baseline=baseline, packed=packed, tail_extra=tail_extra, total=packed + tail_extra,
+                reduction=baseline / (packed + tail_extra))

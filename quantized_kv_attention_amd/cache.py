@@ -170,11 +170,21 @@ class DecodeBuffers:
         self.scores = torch.zeros((B, H, cache.cap), dtype=torch.float32, device=device)
         self.lse = torch.zeros((B, H), dtype=torch.float32, device=device)
         self.max_k = max(1, max_k)
-        self.idx = torch.zeros((B, H, self.max_k), dtype=torch.int32, device=device)
-        self.p_sel = torch.zeros((B, H, self.max_k), dtype=torch.float32, device=device)
-        self.mass = torch.zeros((B, H), dtype=torch.float32, device=device)
+        # one selection per loop: idx/p_sel [R, B*H*k used as B x H x k], mass [R, B, H]
+        self.idx = torch.zeros((R, B * H * self.max_k), dtype=torch.int32, device=device)
+        self.p_sel = torch.zeros((R, B * H * self.max_k), dtype=torch.float32, device=device)
+        self.mass = torch.zeros((R, B, H), dtype=torch.float32, device=device)
+        self.B, self.H = B, H
         nbytes = workspace_bytes(B, H, d, cache.cap, self.max_k)
         self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+    def selection(self, loop: int, k: int):
+        """Views (idx, p_sel, mass) of loop `loop`'s selection of k columns."""
+        r = loop - 1
+        kk = max(k, 1)
+        n = self.B * self.H * kk
+        return (self.idx[r, :n].view(self.B, self.H, kk), self.p_sel[r, :n].view(self.B, self.H, kk),
+                self.mass[r])
 
 
 def k_columns(frac: float, n: int) -> int:
@@ -190,10 +200,9 @@ def decode_loop(cache: LayerCache, bufs: DecodeBuffers, loop: int, q, n_dense: i
         return
     n = cache.n_ctx
     assert k <= bufs.max_k
-    idx = bufs.idx.view(-1)[:cache.B * cache.H * k].view(cache.B, cache.H, k) if k > 0 else bufs.idx
-    ps = bufs.p_sel.view(-1)[:cache.B * cache.H * k].view(cache.B, cache.H, k) if k > 0 else bufs.p_sel
-    select_columns(bufs.scores, bufs.lse, n, k, idx, ps, bufs.mass, None, stream)
-    attn_decode_sparse(cache, loop, q, sm, idx, ps, bufs.mass, k, bufs.o_f32[r - 1], bufs.lse, bufs.scores,
+    idx, ps, mass = bufs.selection(loop, k)
+    select_columns(bufs.scores, bufs.lse, n, k, idx, ps, mass, None, stream)
+    attn_decode_sparse(cache, loop, q, sm, idx, ps, mass, k, bufs.o_f32[r - 1], bufs.lse, bufs.scores,
                        bufs.o[r], bufs.o_f32[r], bufs.ws, stream)
 
 

@@ -98,10 +98,30 @@ __device__ __forceinline__ void vpass_block(const uint8_t* bp, int prt, int rsub
     }
 }
 
+// Merges the nsplit1 partials of one (sequence, head) in split order; threads < D.
+template <int D>
+__device__ __forceinline__ void dense_combine(const float* pp, int nsplit1, int c, uint16_t* o, float* o32,
+                                              float* lse, int bh) {
+    float M = -__builtin_huge_valf();
+    for (int s = 0; s < nsplit1; ++s) M = fmaxf(M, pp[(size_t)s * (D + 2)]);
+    float L = 0.f, a = 0.f;
+    for (int s = 0; s < nsplit1; ++s) {
+        const float e = __expf(pp[(size_t)s * (D + 2)] - M);
+        L = fmaf(pp[(size_t)s * (D + 2) + 1], e, L);
+        a = fmaf(pp[(size_t)s * (D + 2) + 2 + c], e, a);
+    }
+    const float oc = a / L;
+    o32[(size_t)bh * D + c] = oc;
+    if (o) o[(size_t)bh * D + c] = f32_to_bf16_rne(oc);
+    if (c == 0) lse[bh] = M + __logf(L);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                           float sm, float* __restrict__ scores, int ld,
-                                                          float* __restrict__ part, int nsplit, int spb) {
+                                                          float* __restrict__ part, unsigned* __restrict__ counters,
+                                                          int nsplit, int spb, uint16_t* __restrict__ o,
+                                                          float* __restrict__ o32, float* __restrict__ lse) {
     constexpr int LPR = Block<D>::kLpr, RPI = Block<D>::kRpi;
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -275,27 +295,17 @@ __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop,
         out[0] = mx;
         out[1] = lsum;
     }
-}
 
-template <int D>
-__global__ __launch_bounds__(D) void dense_combine_kernel(const float* __restrict__ part, int nsplit1,
-                                                          uint16_t* __restrict__ o, float* __restrict__ o32,
-                                                          float* __restrict__ lse) {
-    const int bh = blockIdx.x;
-    const int c = threadIdx.x;
-    const float* pp = part + (size_t)bh * nsplit1 * (D + 2);
-    float M = -__builtin_huge_valf();
-    for (int s = 0; s < nsplit1; ++s) M = fmaxf(M, pp[(size_t)s * (D + 2)]);
-    float L = 0.f, a = 0.f;
-    for (int s = 0; s < nsplit1; ++s) {
-        const float e = __expf(pp[(size_t)s * (D + 2)] - M);
-        L = fmaf(pp[(size_t)s * (D + 2) + 1], e, L);
-        a = fmaf(pp[(size_t)s * (D + 2) + 2 + c], e, a);
-    }
-    const float oc = a / L;
-    o32[(size_t)bh * D + c] = oc;
-    if (o) o[(size_t)bh * D + c] = f32_to_bf16_rne(oc);
-    if (c == 0) lse[bh] = M + __logf(L);
+    // the last workgroup of this (sequence, head) to finish merges every split
+    __shared__ unsigned last;
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) last = (atomicAdd(&counters[bh], 1u) == (unsigned)nsplit) ? 1u : 0u;
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    if (tid < D) dense_combine<D>(part + (size_t)bh * (nsplit + 1) * (D + 2), nsplit + 1, tid, o, o32, lse, bh);
+    if (tid == 0) atomicExch(&counters[bh], 0u);
 }
 
 DensePlan dense_plan(int B, int H, int n_body) {
@@ -315,23 +325,26 @@ DensePlan dense_plan(int B, int H, int n_body) {
     return pl;
 }
 
+// workspace: per-(sequence, head) counters first, then the split partials
+size_t ws_counter_bytes(int B, int H) { return (((size_t)B * H * sizeof(unsigned)) + 255) & ~(size_t)255; }
+
 size_t dense_ws_bytes(int B, int H, int D, int n_body) {
     const DensePlan pl = dense_plan(B, H, n_body);
-    return (size_t)B * H * (pl.nsplit + 1) * (D + 2) * sizeof(float);
+    return ws_counter_bytes(B, H) + (size_t)B * H * (pl.nsplit + 1) * (D + 2) * sizeof(float);
 }
 
 int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, uint16_t* o, float* o32,
                  float* scores, int ld, float* lse, void* ws, hipStream_t st) {
     const DensePlan pl = dense_plan(ca.B, ca.H, ca.n_body);
-    float* part = reinterpret_cast<float*>(ws);
+    unsigned* counters = reinterpret_cast<unsigned*>(ws);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_counter_bytes(ca.B, ca.H));
     dim3 grid(pl.nsplit + 1, ca.H, ca.B);
-    if (D == 128) {
-        dense_split_kernel<128><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
-        dense_combine_kernel<128><<<ca.B * ca.H, 128, 0, st>>>(part, pl.nsplit + 1, o, o32, lse);
-    } else {
-        dense_split_kernel<64><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
-        dense_combine_kernel<64><<<ca.B * ca.H, 64, 0, st>>>(part, pl.nsplit + 1, o, o32, lse);
-    }
+    if (D == 128)
+        dense_split_kernel<128><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, counters, pl.nsplit, pl.spb,
+                                                      o, o32, lse);
+    else
+        dense_split_kernel<64><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, counters, pl.nsplit, pl.spb,
+                                                     o, o32, lse);
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
 }
 

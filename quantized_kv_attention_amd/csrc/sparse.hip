@@ -18,12 +18,53 @@ namespace qkv {
 
 constexpr int kChunk = 64;
 
+// Merges the chunk partials of one (sequence, head): o = o_prev + m * U / L - W, then
+// shifts the selected scores onto the previous lse scale.  nthreads >= D threads.
+template <int D>
+__device__ __forceinline__ void sparse_combine(const float* pp, int nchunk, float m, const float* o_prev,
+                                               float lse_prev, const int32_t* id, int k, float* srow, int ld,
+                                               uint16_t* o, float* o32, int bh, int tid, int nthreads) {
+    float M = -__builtin_huge_valf();
+    for (int s = 0; s < nchunk; ++s) M = fmaxf(M, pp[(size_t)s * (2 + 2 * D)]);
+    float L = 0.f;
+    for (int s = 0; s < nchunk; ++s) L = fmaf(pp[(size_t)s * (2 + 2 * D) + 1], __expf(pp[(size_t)s * (2 + 2 * D)] - M), L);
+    if (tid < D) {
+        const int c = tid;
+        float u = 0.f, w = 0.f;
+        for (int s = 0; s < nchunk; ++s) {
+            const float* q = pp + (size_t)s * (2 + 2 * D);
+            u = fmaf(q[2 + c], __expf(q[0] - M), u);
+            w += q[2 + D + c];
+        }
+        const float oc = o_prev[(size_t)bh * D + c] + m * (u / L) - w;
+        o32[(size_t)bh * D + c] = oc;
+        if (o) o[(size_t)bh * D + c] = f32_to_bf16_rne(oc);
+    }
+    const float shift = lse_prev + __logf(m) - (M + __logf(L));
+    for (int i = tid; i < k; i += nthreads) {
+        const int j = id[i];
+        if (j >= 0 && j < ld) srow[j] += shift;
+    }
+}
+
+// k == 0: the output is the previous loop's output
+template <int D>
+__global__ __launch_bounds__(D) void sparse_copy_kernel(const float* o_prev, uint16_t* __restrict__ o, float* o32) {
+    const int bh = blockIdx.x, c = threadIdx.x;
+    const float v = o_prev[(size_t)bh * D + c];
+    o32[(size_t)bh * D + c] = v;
+    if (o) o[(size_t)bh * D + c] = f32_to_bf16_rne(v);
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void sparse_chunk_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                           float sm, const int32_t* __restrict__ idx,
                                                           const float* __restrict__ p_sel, int k,
                                                           float* __restrict__ scores, int ld,
-                                                          float* __restrict__ part, int nchunk) {
+                                                          float* __restrict__ part, unsigned* __restrict__ counters,
+                                                          int nchunk, const float* __restrict__ mass,
+                                                          const float* o_prev, const float* __restrict__ lse,
+                                                          uint16_t* __restrict__ o, float* o32) {
     constexpr int LPR = Block<D>::kLpr, RPI = Block<D>::kRpi, ROUNDS = kChunk / RPI;
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, prt = lane % LPR, rsub = lane / LPR;
@@ -147,66 +188,47 @@ __global__ __launch_bounds__(64) void sparse_chunk_kernel(CacheArg ca, int loop,
         out[0] = mxw;
         out[1] = lw;
     }
-}
 
-template <int D>
-__global__ __launch_bounds__(D) void sparse_combine_kernel(const float* __restrict__ part, int nchunk,
-                                                           const float* __restrict__ mass,
-                                                           const float* o_prev, const float* __restrict__ lse,
-                                                           const int32_t* __restrict__ idx, int k,
-                                                           float* __restrict__ scores, int ld,
-                                                           uint16_t* __restrict__ o, float* o32) {
-    const int bh = blockIdx.x, c = threadIdx.x;
-    const float op = o_prev[(size_t)bh * D + c];
-    float oc = op;
-    if (nchunk > 0) {
-        const float* pp = part + (size_t)bh * nchunk * (2 + 2 * D);
-        float M = -__builtin_huge_valf();
-        for (int s = 0; s < nchunk; ++s) M = fmaxf(M, pp[(size_t)s * (2 + 2 * D)]);
-        float L = 0.f, u = 0.f, w = 0.f;
-        for (int s = 0; s < nchunk; ++s) {
-            const float* q = pp + (size_t)s * (2 + 2 * D);
-            const float e = __expf(q[0] - M);
-            L = fmaf(q[1], e, L);
-            u = fmaf(q[2 + c], e, u);
-            w += q[2 + D + c];
-        }
-        const float m = mass[bh];
-        oc = op + m * (u / L) - w;
-        const float shift = lse[bh] + __logf(m) - (M + __logf(L));
-        __syncthreads();
-        for (int i = c; i < k; i += D) {
-            const int j = idx[(size_t)bh * k + i];
-            if (j >= 0 && j < ld) scores[(size_t)bh * ld + j] += shift;
-        }
+    // the last chunk of this (sequence, head) to finish merges every chunk
+    __threadfence();
+    unsigned last = 0;
+    if (lane == 0) last = (atomicAdd(&counters[bh], 1u) == (unsigned)(nchunk - 1)) ? 1u : 0u;
+    last = __shfl(last, 0, 64);
+    if (!last) return;
+    __threadfence();
+    for (int t0 = 0; t0 < D; t0 += 64) {
+        // each pass of 64 lanes covers 64 channels; the score shift is applied once
+        sparse_combine<D>(part + (size_t)bh * nchunk * (2 + 2 * D), nchunk, mass[bh], o_prev, lse[bh], id,
+                          t0 == 0 ? k : 0, scores + (size_t)bh * ld, ld, o, o32, bh, t0 + lane, 64);
     }
-    o32[(size_t)bh * D + c] = oc;
-    if (o) o[(size_t)bh * D + c] = f32_to_bf16_rne(oc);
+    if (lane == 0) atomicExch(&counters[bh], 0u);
 }
 
 size_t sparse_ws_bytes(int B, int H, int D, int k) {
     const int nchunk = (k + kChunk - 1) / kChunk;
-    return (size_t)B * H * nchunk * (2 + 2 * D) * sizeof(float);
+    return ws_counter_bytes(B, H) + (size_t)B * H * nchunk * (2 + 2 * D) * sizeof(float);
 }
 
 int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, const int32_t* idx,
                   const float* p_sel, const float* mass, int k, const float* o_prev, const float* lse,
                   float* scores, int ld, uint16_t* o, float* o32, void* ws, hipStream_t st) {
     const int nchunk = (k + kChunk - 1) / kChunk;
-    float* part = reinterpret_cast<float*>(ws);
-    if (nchunk > 0) {
-        dim3 grid(nchunk, ca.H, ca.B);
+    if (nchunk == 0) {
         if (D == 128)
-            sparse_chunk_kernel<128><<<grid, 64, 0, st>>>(ca, loop, q, sm, idx, p_sel, k, scores, ld, part, nchunk);
+            sparse_copy_kernel<128><<<ca.B * ca.H, 128, 0, st>>>(o_prev, o, o32);
         else
-            sparse_chunk_kernel<64><<<grid, 64, 0, st>>>(ca, loop, q, sm, idx, p_sel, k, scores, ld, part, nchunk);
+            sparse_copy_kernel<64><<<ca.B * ca.H, 64, 0, st>>>(o_prev, o, o32);
+        return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
     }
+    unsigned* counters = reinterpret_cast<unsigned*>(ws);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_counter_bytes(ca.B, ca.H));
+    dim3 grid(nchunk, ca.H, ca.B);
     if (D == 128)
-        sparse_combine_kernel<128><<<ca.B * ca.H, 128, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, k, scores, ld,
-                                                                o, o32);
+        sparse_chunk_kernel<128><<<grid, 64, 0, st>>>(ca, loop, q, sm, idx, p_sel, k, scores, ld, part, counters,
+                                                      nchunk, mass, o_prev, lse, o, o32);
     else
-        sparse_combine_kernel<64><<<ca.B * ca.H, 64, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, k, scores, ld, o,
-                                                              o32);
+        sparse_chunk_kernel<64><<<grid, 64, 0, st>>>(ca, loop, q, sm, idx, p_sel, k, scores, ld, part, counters,
+                                                     nchunk, mass, o_prev, lse, o, o32);
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
 }
 

@@ -188,3 +188,27 @@ def active_positions(act_r: np.ndarray, p0: int, p1: int):
         out[b, :pos.size] = pos
         cnt[b] = pos.size
     return out, cnt
+
+
+def gen_layer_torch(w: Workload, layer: int, device="cuda", n: int | None = None):
+    """Same recipe as gen_layer, drawn with torch's generator on the GPU (for the large
+    caches of the bench; the masks come from gen_masks).  Returns K[r], V[r] as bf16
+    tensors [B, H, n, d] and act[r] as bool arrays [B, n]."""
+    import torch
+    n = w.n if n is None else n
+    act = gen_masks(w, n)
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed * 1000 + layer)
+    shape = (w.B, w.H, n, w.d)
+    K = [torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)]
+    V = [torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)]
+    for r in range(1, w.R):
+        a = torch.from_numpy(act[r]).to(device)[:, None, :, None]
+        sig = float(w.sigma[r - 1])
+        nk = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        K.append(torch.where(a, (K[r - 1].float() + sig * nk).to(torch.bfloat16), K[r - 1]))
+        del nk
+        nv = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        V.append(torch.where(a, (V[r - 1].float() + sig * nv).to(torch.bfloat16), V[r - 1]))
+        del nv
+    return K, V, act

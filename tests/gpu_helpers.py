@@ -135,10 +135,10 @@ class Pair:
             snap["scores"] = bufs.scores[:, :, :n].cpu().numpy().copy()
             snap["lse"] = bufs.lse.cpu().numpy().copy()
             if loop > n_dense and k > 0:
-                kk = k
-                snap["idx"] = bufs.idx.view(-1)[:c.B * c.H * kk].view(c.B, c.H, kk).cpu().numpy().copy()
-                snap["p_sel"] = bufs.p_sel.view(-1)[:c.B * c.H * kk].view(c.B, c.H, kk).cpu().numpy().copy()
-                snap["mass"] = bufs.mass.cpu().numpy().copy()
+                idx, ps, mass = bufs.selection(loop, k)
+                snap["idx"] = idx.cpu().numpy().copy()
+                snap["p_sel"] = ps.cpu().numpy().copy()
+                snap["mass"] = mass.cpu().numpy().copy()
             snaps.append(snap)
         return snaps
 

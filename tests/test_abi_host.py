@@ -101,3 +101,19 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(qkv, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError):
         qkv.lib()
+
+
+def test_host_buffers_and_descriptor_cpu():
+    # allocation and descriptor bookkeeping run without a GPU (host memory stands in)
+    from quantized_kv_attention_amd import cache as qcache
+    c = qcache.LayerCache(2, 3, 128, 4, 512, device="cpu")
+    assert c.dense == [True, True, False, False]
+    assert c.desc.plane[0].n_blocks == 8 and c.desc.plane[2].dense == 0
+    assert c.desc.plane[2].rowmap == c.rowmap[2].data_ptr()
+    assert c.planes[0].numel() == 2 * 3 * 8 * qkv.block_bytes(128)
+    b = qcache.DecodeBuffers(c, max_k=50, device="cpu")
+    idx, ps, m = b.selection(3, 50)
+    assert idx.shape == (2, 3, 50) and ps.shape == (2, 3, 50) and m.shape == (2, 3)
+    assert b.ws.numel() >= qkv.workspace_bytes(2, 3, 128, 512, 50)
+    a, n = c._active_lists(2, 0, 64)
+    assert a.shape == (2, 64) and n.shape == (2,)
