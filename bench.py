@@ -82,8 +82,8 @@ def main():
         bufs = qcache.DecodeBuffers(c, max_k=k)
         qs = [dev(x) for x in synth.gen_queries(w, 1000 + l)]
         kn, vn = synth.gen_new_token(w, 1000 + l)
-        kn = [dev(x).view(w.B, w.H, 1, w.d) for x in kn]
-        vn = [dev(x).view(w.B, w.H, 1, w.d) for x in vn]
+        kn = torch.stack([dev(x).view(w.B, w.H, 1, w.d) for x in kn])  # [R, B, H, 1, d]
+        vn = torch.stack([dev(x).view(w.B, w.H, 1, w.d) for x in vn])
         c.act[:, :, n] = True
         flush = []
         for r in range(w.R):
@@ -110,8 +110,7 @@ def main():
                         qkv.kv_encode_loop(c, r + 1, nb, 64)
                     else:
                         qkv.kv_encode_loop(c, r + 1, nb, 64, f[0], f[1])
-            for r in range(w.R):
-                qkv.kv_append_tail(c, r + 1, n, ly["kn"][r], ly["vn"][r])
+            qkv.kv_append_tail(c, 0, n, ly["kn"], ly["vn"])  # every loop in one launch
         for loop in range(1, w.R + 1):
             for ly in layers:
                 qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k)

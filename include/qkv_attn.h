@@ -141,6 +141,7 @@ int kv_encode_loop(const qkv_cache* cache, int loop, int pos0, int n_pos,
  * kv_append_tail - writes n_rows consecutive positions pos0.. of loop `loop` into the BF16
  * tail ring [PyPI Configuration: 64-token BF16 residual tail].
  *   k, v: device bf16 [batch][heads][n_rows][head_dim].  1 <= n_rows <= 128.
+ *   loop == 0 writes every loop in one launch; k, v are then [n_loops][batch][heads][n_rows][head_dim].
  */
 int kv_append_tail(const qkv_cache* cache, int loop, int pos0, int n_rows,
                    const uint16_t* k, const uint16_t* v, void* stream);

@@ -123,8 +123,9 @@ def kv_encode_loop(cache, loop, pos0, n_pos, act_pos=None, n_act=None, k_src=Non
 
 
 def kv_append_tail(cache, loop, pos0, k, v, stream=None):
-    """Writes bf16 rows k, v [B, H, n_rows, d] at positions pos0.. of `loop`'s BF16 tail."""
-    st = lib().kv_append_tail(ctypes.byref(cache.desc), loop, pos0, k.shape[2], _ptr(k), _ptr(v), _stream(stream))
+    """Writes bf16 rows k, v [B, H, n_rows, d] at positions pos0.. of `loop`'s BF16 tail
+    (loop 0: every loop, k, v [R, B, H, n_rows, d])."""
+    st = lib().kv_append_tail(ctypes.byref(cache.desc), loop, pos0, k.shape[-2], _ptr(k), _ptr(v), _stream(stream))
     _check("kv_append_tail", st)
 
 

@@ -153,10 +153,13 @@ class LayerCache:
                     act_pos, n_act = self._active_lists(r, nb_old, nb_old + GROUP)
                     kv_encode_loop(self, r + 1, nb_old, GROUP, torch.from_numpy(act_pos).to(self.device),
                                    torch.from_numpy(n_act).to(self.device), stream=stream)
-        for r in range(self.R):
-            self.act[r, :, t] = True
-            kv_append_tail(self, r + 1, t, k_new[r].reshape(self.B, self.H, 1, self.d),
-                           v_new[r].reshape(self.B, self.H, 1, self.d), stream=stream)
+        self.act[:, :, t] = True
+        if torch.is_tensor(k_new) and k_new.dim() == 5:
+            kv_append_tail(self, 0, t, k_new, v_new, stream=stream)  # [R, B, H, 1, d], one launch
+        else:
+            ks = torch.stack([x.reshape(self.B, self.H, 1, self.d) for x in k_new])
+            vs = torch.stack([x.reshape(self.B, self.H, 1, self.d) for x in v_new])
+            kv_append_tail(self, 0, t, ks, vs, stream=stream)
         self.n_ctx = t + 1
 
 

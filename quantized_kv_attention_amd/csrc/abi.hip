@@ -128,10 +128,11 @@ int kv_append_tail(const qkv_cache* cache, int loop, int pos0, int n_rows, const
     CacheArg a;
     int st = make_arg(cache, &a);
     if (st) return st;
-    if (loop < 1 || loop > cache->n_loops) return QKV_EINVAL;
+    if (loop < 0 || loop > cache->n_loops) return QKV_EINVAL;
     if (n_rows < 1 || n_rows > QKV_TAIL_SLOTS || pos0 < 0) return QKV_EINVAL;
     if ((long)pos0 + n_rows > cache->cap_ctx) return QKV_ECAPACITY;
     if (!k || !v || !aligned16(k) || !aligned16(v)) return QKV_EINVAL;
+    if (loop == 0) return launch_append_all(a, cache->head_dim, pos0, n_rows, k, v, to_stream(stream));
     return launch_append(cache->batch, cache->heads, cache->head_dim, pos0, n_rows, k, v, cache->tail_k[loop - 1],
                          cache->tail_v[loop - 1], to_stream(stream));
 }

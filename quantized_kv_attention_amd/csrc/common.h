@@ -122,4 +122,165 @@ __device__ __forceinline__ void unpack32_codes(const uint4 w, float* c) {
     }
 }
 
+
+// ---- cross-lane helpers (DPP: no LDS traffic) ----
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;   // row_ror:4
+constexpr int kRowRor8 = 0x128;   // row_ror:8
+
+// sum over the LPR consecutive lanes of a row group (LPR = 2 or 4)
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp<kQuadXor1>(v);
+    if (LPR == 4) v += dpp<kQuadXor2>(v);
+    return v;
+}
+// sum over the whole wave, result in every lane
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp<kQuadXor1>(v);
+    v += dpp<kQuadXor2>(v);
+    v += dpp<kRowRor4>(v);
+    v += dpp<kRowRor8>(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// ---- nibble codes to floats through the FP8 converter ----
+// A byte b in [0, 15] read as OCP FP8 E4M3 (bias 7) is exactly b * 2^-9: codes 0-7 are the
+// subnormals m * 2^-9, codes 8-15 the first normal binade (8 + m) * 2^-9.  Masking a code
+// word to its low (or high) nibbles and converting two bytes per instruction turns 8 codes
+// into floats with 7 instructions; callers fold the 2^9 into their multiplier.
+constexpr float kFp8CodeScale = 512.0f;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void codes8_fp8(uint32_t w, float* c) {
+    const uint32_t lo = w & 0x0F0F0F0Fu;          // channels 0, 2, 4, 6
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // channels 1, 3, 5, 7
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+    const f32x2 e = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+    c[0] = a.x; c[2] = a.y; c[4] = b.x; c[6] = b.y;
+    c[1] = e.x; c[3] = e.y; c[5] = f.x; c[7] = f.y;
+}
+
+// sum_c q[c] * code[c] * 2^-9 over the 32 codes of 16 bytes
+__device__ __forceinline__ float dot32_fp8(const uint4 w, const float* q) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float c[8];
+        codes8_fp8(ws[k], c);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            a0 = fmaf(c[e], q[8 * k + e], a0);
+            a1 = fmaf(c[e + 1], q[8 * k + e + 1], a1);
+        }
+    }
+    return a0 + a1;
+}
+
+// acc[c] += wt * code[c] * 2^-9 for the 32 codes of 16 bytes
+__device__ __forceinline__ void axpy32_fp8(const uint4 w, float wt, float* acc) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float c[8];
+        codes8_fp8(ws[k], c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[8 * k + e] = fmaf(c[e], wt, acc[8 * k + e]);
+    }
+}
+
+// Merge of split-softmax partials of one (sequence, head), laid out as nsplit records of
+// `stride` floats: [max, sum, a[0..D), (b[0..D))].  Thread t owns channel t % D and the
+// records s = t / D (mod NT / D); it loads all of its records' fields first (one memory
+// latency), then the global max, the rescale weights and the sums are formed, and the
+// per-thread sums are added in record-group order (deterministic).  Returns
+// L = sum_s sum_s * exp(max_s - M) and M in *gmax; writes a[c] (rescaled) and, if has_b,
+// b[c] (plain sums) into out_a / out_b (LDS), valid for every thread after the call.
+template <int D, int NT, int NPER>
+__device__ __forceinline__ float merge_partials(const float* pp, int nsplit, int stride, bool has_b, float* red,
+                                                float* out_a, float* out_b, float* grp /* [NT] */, float* gmax) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NW = NT / 64;
+    constexpr int G = NT / D;
+    const int c = tid % D, g = tid / D;
+    float mv[NPER], lv[NPER], av[NPER], bv[NPER];
+#pragma unroll
+    for (int e = 0; e < NPER; ++e) {
+        const int s = g + e * G;
+        mv[e] = -__builtin_huge_valf();
+        lv[e] = av[e] = bv[e] = 0.f;
+        if (s < nsplit) {
+            const float* q = pp + (size_t)s * stride;
+            mv[e] = q[0];
+            lv[e] = q[1];
+            av[e] = q[2 + c];
+            if (has_b) bv[e] = q[2 + D + c];
+        }
+    }
+    float m = -__builtin_huge_valf();
+#pragma unroll
+    for (int e = 0; e < NPER; ++e) m = fmaxf(m, mv[e]);
+    for (int s = g + NPER * G; s < nsplit; s += G) m = fmaxf(m, pp[(size_t)s * stride]);
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    float M = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
+    *gmax = M;
+    float a = 0.f, b = 0.f, l = 0.f;
+#pragma unroll
+    for (int e = 0; e < NPER; ++e) {
+        const float w = (mv[e] == -__builtin_huge_valf()) ? 0.f : __expf(mv[e] - M);
+        a = fmaf(av[e], w, a);
+        l = fmaf(lv[e], w, l);
+        b += bv[e];
+    }
+    for (int s = g + NPER * G; s < nsplit; s += G) {
+        const float* q = pp + (size_t)s * stride;
+        const float w = (q[0] == -__builtin_huge_valf()) ? 0.f : __expf(q[0] - M);
+        a = fmaf(q[2 + c], w, a);
+        l = fmaf(q[1], w, l);
+        if (has_b) b += q[2 + D + c];
+    }
+    __syncthreads();
+    grp[tid] = a;
+    if (c == 0) red[g] = l;
+    __syncthreads();
+    float L = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) L += red[gg];
+    if (tid < D) {
+        float t = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) t += grp[gg * D + tid];
+        out_a[tid] = t;
+    }
+    if (has_b) {
+        __syncthreads();
+        grp[tid] = b;
+        __syncthreads();
+        if (tid < D) {
+            float t = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < G; ++gg) t += grp[gg * D + tid];
+            out_b[tid] = t;
+        }
+    }
+    __syncthreads();
+    return L;
+}
+
 }  // namespace qkv

@@ -16,6 +16,7 @@
 namespace qkv {
 
 constexpr int kMaxSpb = 16;  // 64-position blocks per split, at most
+constexpr int kMaxPre = 2;   // leading dense planes whose folded queries are prepared per split
 
 __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -23,7 +24,6 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D>
 __device__ __forceinline__ float block_reduce_max(float v, float* red) {
     v = wave_max(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -32,7 +32,6 @@ __device__ __forceinline__ float block_reduce_max(float v, float* red) {
     __syncthreads();
     return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
-template <int D>
 __device__ __forceinline__ float block_reduce_sum(float v, float* red) {
     v = wave_sum(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -42,7 +41,22 @@ __device__ __forceinline__ float block_reduce_sum(float v, float* red) {
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// K pass over one 64-slot block: calls emit(row, partial_logit) on one lane per row.
+// Folded query of one key block: qp[c] = 2^9 * q[c] * s[c] (LDS), returns sum_c q[c] z[c].
+template <int D>
+__device__ __forceinline__ float fold_query(const uint8_t* bp, const float* qsh, float* qp, int lane) {
+    const float* km = reinterpret_cast<const float*>(bp + Block<D>::kKm);
+    float bias = 0.f;
+#pragma unroll
+    for (int c = lane; c < D; c += 64) {
+        const float qc = qsh[c];
+        qp[c] = qc * km[c] * kFp8CodeScale;
+        bias = fmaf(qc, km[D + c], bias);
+    }
+    return wave_sum_dpp(bias);
+}
+
+// K pass over one 64-slot block with the folded query computed here (planes that are not
+// prepared per split): calls emit(row, partial_logit) on one lane per row.
 template <int D, typename Emit>
 __device__ __forceinline__ void kpass_block(const uint8_t* bp, const float* qsh, float* qp_lds, int lane, int prt,
                                             int rsub, Emit emit) {
@@ -51,15 +65,7 @@ __device__ __forceinline__ void kpass_block(const uint8_t* bp, const float* qsh,
 #pragma unroll
     for (int it = 0; it < NLD; ++it)
         w[it] = *reinterpret_cast<const uint4*>(bp + Block<D>::kKc + (rsub + RPI * it) * (D / 2) + prt * 16);
-    const float* km = reinterpret_cast<const float*>(bp + Block<D>::kKm);
-    float bias = 0.f;
-#pragma unroll
-    for (int c = lane; c < D; c += 64) {
-        const float qc = qsh[c];
-        qp_lds[c] = qc * km[c];
-        bias = fmaf(qc, km[D + c], bias);
-    }
-    bias = wave_sum(bias);
+    const float bias = fold_query<D>(bp, qsh, qp_lds, lane);
     wave_sync_lds();
     float qp[32];
 #pragma unroll
@@ -70,9 +76,7 @@ __device__ __forceinline__ void kpass_block(const uint8_t* bp, const float* qsh,
     wave_sync_lds();
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
-        float v = dot32_codes(w[it], qp);
-#pragma unroll
-        for (int m = 1; m < LPR; m <<= 1) v += __shfl_xor(v, m, 64);
+        const float v = group_sum<LPR>(dot32_fp8(w[it], qp));
         if (prt == 0) emit(rsub + RPI * it, v + bias);
     }
 }
@@ -94,35 +98,15 @@ __device__ __forceinline__ void vpass_block(const uint8_t* bp, int prt, int rsub
     for (int it = 0; it < NLD; ++it) {
         const float pw = weight(rsub + RPI * it);
         vb = fmaf(pw, m[it].y, vb);
-        axpy32_codes(w[it], pw * m[it].x, acc);
+        axpy32_fp8(w[it], pw * m[it].x * kFp8CodeScale, acc);
     }
-}
-
-// Merges the nsplit1 partials of one (sequence, head) in split order; threads < D.
-template <int D>
-__device__ __forceinline__ void dense_combine(const float* pp, int nsplit1, int c, uint16_t* o, float* o32,
-                                              float* lse, int bh) {
-    float M = -__builtin_huge_valf();
-    for (int s = 0; s < nsplit1; ++s) M = fmaxf(M, pp[(size_t)s * (D + 2)]);
-    float L = 0.f, a = 0.f;
-    for (int s = 0; s < nsplit1; ++s) {
-        const float e = __expf(pp[(size_t)s * (D + 2)] - M);
-        L = fmaf(pp[(size_t)s * (D + 2) + 1], e, L);
-        a = fmaf(pp[(size_t)s * (D + 2) + 2 + c], e, a);
-    }
-    const float oc = a / L;
-    o32[(size_t)bh * D + c] = oc;
-    if (o) o[(size_t)bh * D + c] = f32_to_bf16_rne(oc);
-    if (c == 0) lse[bh] = M + __logf(L);
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                           float sm, float* __restrict__ scores, int ld,
-                                                          float* __restrict__ part, unsigned* __restrict__ counters,
-                                                          int nsplit, int spb, uint16_t* __restrict__ o,
-                                                          float* __restrict__ o32, float* __restrict__ lse) {
-    constexpr int LPR = Block<D>::kLpr, RPI = Block<D>::kRpi;
+                                                          float* __restrict__ part, int nsplit, int spb) {
+    constexpr int LPR = Block<D>::kLpr, RPI = Block<D>::kRpi, NLD = 64 / RPI;
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int prt = lane % LPR, rsub = lane / LPR;
@@ -130,6 +114,8 @@ __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop,
 
     __shared__ float qsh[D];
     __shared__ float logit[kMaxSpb * 64];
+    __shared__ float qpre[kMaxPre][kMaxSpb][D];
+    __shared__ float bpre[kMaxPre][kMaxSpb];
     __shared__ float qps[4][D];
     __shared__ float red[4];
     __shared__ float ored[4][D];
@@ -169,8 +155,7 @@ __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop,
                     }
                 }
             }
-#pragma unroll
-            for (int m = 1; m < LPR; m <<= 1) v += __shfl_xor(v, m, 64);
+            v = group_sum<LPR>(v);
             if (prt == 0 && i < T) logit[i] = v;
         }
         __syncthreads();
@@ -179,14 +164,14 @@ __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop,
             srow[ca.n_body + i] = logit[i];
             lm = fmaxf(lm, logit[i]);
         }
-        mx = block_reduce_max<D>(lm, red);
+        mx = block_reduce_max(lm, red);
         float ls = 0.f;
         for (int i = tid; i < T; i += 256) {
             const float pv = __expf(logit[i] - mx);
             logit[i] = pv;
             ls += pv;
         }
-        lsum = block_reduce_sum<D>(ls, red);
+        lsum = block_reduce_sum(ls, red);
         for (int i0 = wave * RPI; i0 < T; i0 += 4 * RPI) {
             const int i = i0 + rsub;
             if (i < T) {
@@ -208,11 +193,62 @@ __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop,
         // ---- body split: blocks [blk0, blk1) ----
         const int nblk = ca.n_body / 64;
         const int blk0 = s * spb, blk1 = min(blk0 + spb, nblk);
-        const int j0 = blk0 * 64, L = (blk1 - blk0) * 64;
+        const int nb = blk1 - blk0;
+        const int j0 = blk0 * 64, L = nb * 64;
         const int nstart = ca.cap_ctx / 64 + 1;
-        for (int i = tid; i < L; i += 256) logit[i] = 0.f;
+        {
+        // leading dense planes are read block by block together; their folded queries are
+        // prepared once per split (one wave per (plane, block))
+        int npre = 0;
+        while (npre < kMaxPre && npre < loop && ca.p[npre].dense) ++npre;
+        for (int i = wave; i < npre * nb; i += 4) {
+            const int p = i / nb, bb = i % nb;
+            const float bias = fold_query<D>(block_ptr<D>(ca.p[p], ca.H, b, h, blk0 + bb), qsh, qpre[p][bb], lane);
+            if (lane == 0) bpre[p][bb] = bias;
+        }
         __syncthreads();
-        for (int p = 0; p < loop; ++p) {
+
+        // K pass, prepared planes: logits of every row of the block summed over the planes
+        for (int blk = blk0 + wave; blk < blk1; blk += 4) {
+            const int bb = blk - blk0;
+            uint4 w[kMaxPre][NLD];
+#pragma unroll
+            for (int p = 0; p < kMaxPre; ++p) {
+                if (p < npre) {
+                    const uint8_t* bp = block_ptr<D>(ca.p[p], ca.H, b, h, blk);
+#pragma unroll
+                    for (int it = 0; it < NLD; ++it)
+                        w[p][it] = *reinterpret_cast<const uint4*>(bp + Block<D>::kKc + (rsub + RPI * it) * (D / 2) +
+                                                                   prt * 16);
+                }
+            }
+            float lg[NLD];
+#pragma unroll
+            for (int it = 0; it < NLD; ++it) lg[it] = 0.f;
+            float bias = 0.f;
+#pragma unroll
+            for (int p = 0; p < kMaxPre; ++p) {
+                if (p < npre) {
+                    float qp[32];
+#pragma unroll
+                    for (int k = 0; k < 32; k += 4) {
+                        const float4 t = *reinterpret_cast<const float4*>(&qpre[p][bb][32 * prt + k]);
+                        qp[k] = t.x; qp[k + 1] = t.y; qp[k + 2] = t.z; qp[k + 3] = t.w;
+                    }
+#pragma unroll
+                    for (int it = 0; it < NLD; ++it) lg[it] += dot32_fp8(w[p][it], qp);
+                    bias += bpre[p][bb];
+                }
+            }
+#pragma unroll
+            for (int it = 0; it < NLD; ++it) {
+                const float v = group_sum<LPR>(lg[it]);
+                if (prt == 0) logit[bb * 64 + rsub + RPI * it] = v + bias;
+            }
+        }
+        __syncthreads();
+        // K pass, remaining planes (sparse planes, or dense planes beyond the prepared ones)
+        for (int p = npre; p < loop; ++p) {
             const PlaneArg& P = ca.p[p];
             if (P.dense) {
                 for (int blk = blk0 + wave; blk < blk1; blk += 4) {
@@ -242,15 +278,47 @@ __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop,
             srow[j0 + i] = logit[i];
             lm = fmaxf(lm, logit[i]);
         }
-        mx = block_reduce_max<D>(lm, red);
+        mx = block_reduce_max(lm, red);
         float ls = 0.f;
         for (int i = tid; i < L; i += 256) {
             const float pv = __expf(logit[i] - mx);
             logit[i] = pv;
             ls += pv;
         }
-        lsum = block_reduce_sum<D>(ls, red);
-        for (int p = 0; p < loop; ++p) {
+        lsum = block_reduce_sum(ls, red);
+
+        // V pass, prepared planes: every plane's codes of the block loaded together
+        for (int blk = blk0 + wave; blk < blk1; blk += 4) {
+            const int bb = blk - blk0;
+            uint4 w[kMaxPre][NLD];
+            float2 m[kMaxPre][NLD];
+#pragma unroll
+            for (int p = 0; p < kMaxPre; ++p) {
+                if (p < npre) {
+                    const uint8_t* bp = block_ptr<D>(ca.p[p], ca.H, b, h, blk);
+#pragma unroll
+                    for (int it = 0; it < NLD; ++it) {
+                        const int row = rsub + RPI * it;
+                        w[p][it] = *reinterpret_cast<const uint4*>(bp + Block<D>::kVc + row * (D / 2) + prt * 16);
+                        m[p][it] = *reinterpret_cast<const float2*>(bp + Block<D>::kVm +
+                                                                    (row * (D / 64) + (prt >> 1)) * 8);
+                    }
+                }
+            }
+#pragma unroll
+            for (int it = 0; it < NLD; ++it) {
+                const float pw = logit[bb * 64 + rsub + RPI * it];
+#pragma unroll
+                for (int p = 0; p < kMaxPre; ++p) {
+                    if (p < npre) {
+                        vb = fmaf(pw, m[p][it].y, vb);
+                        axpy32_fp8(w[p][it], pw * m[p][it].x * kFp8CodeScale, acc);
+                    }
+                }
+            }
+        }
+        // V pass, remaining planes
+        for (int p = npre; p < loop; ++p) {
             const PlaneArg& P = ca.p[p];
             if (P.dense) {
                 for (int blk = blk0 + wave; blk < blk1; blk += 4) {
@@ -276,14 +344,38 @@ __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop,
                 }
             }
         }
+        }  // general path
     }
 
     // reduce the per-lane accumulators over the rows of the wave, then over waves
 #pragma unroll
-    for (int m = LPR; m < 64; m <<= 1) {
-#pragma unroll
-        for (int k = 0; k < 32; ++k) acc[k] += __shfl_xor(acc[k], m, 64);
-        vb += __shfl_xor(vb, m, 64);
+    for (int k = 0; k < 32; ++k) {
+        float v = acc[k];
+        if (LPR == 4) {
+            v += dpp<kRowRor4>(v);   // lanes of a 16-lane row with the same channel part
+            v += dpp<kRowRor8>(v);
+        } else {
+            v += dpp<kQuadXor2>(v);  // LPR 2: rows of a quad
+            v += dpp<kRowRor4>(v);
+            v += dpp<kRowRor8>(v);
+        }
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        acc[k] = v;
+    }
+    {
+        float v = vb;
+        if (LPR == 4) {
+            v += dpp<kRowRor4>(v);
+            v += dpp<kRowRor8>(v);
+        } else {
+            v += dpp<kQuadXor2>(v);
+            v += dpp<kRowRor4>(v);
+            v += dpp<kRowRor8>(v);
+        }
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        vb = v;
     }
     if (rsub == 0) {
 #pragma unroll
@@ -295,17 +387,31 @@ __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop,
         out[0] = mx;
         out[1] = lsum;
     }
+}
 
-    // the last workgroup of this (sequence, head) to finish merges every split
-    __shared__ unsigned last;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) last = (atomicAdd(&counters[bh], 1u) == (unsigned)nsplit) ? 1u : 0u;
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    if (tid < D) dense_combine<D>(part + (size_t)bh * (nsplit + 1) * (D + 2), nsplit + 1, tid, o, o32, lse, bh);
-    if (tid == 0) atomicExch(&counters[bh], 0u);
+// Second kernel of the reader: merges the splits of each (sequence, head) in split order.
+// (A kernel boundary publishes the partials; a per-workgroup device-scope fence in the
+// split kernel would write back and invalidate L2 once per workgroup.)
+constexpr int kCombineThreads = 1024;
+
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void dense_combine_kernel(const float* __restrict__ part, int nsplit1,
+                                                                        uint16_t* __restrict__ o,
+                                                                        float* __restrict__ o32,
+                                                                        float* __restrict__ lse) {
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    __shared__ float red[kCombineThreads / 64];
+    __shared__ float oa[D];
+    __shared__ float grp[kCombineThreads];
+    const float* pp = part + (size_t)bh * nsplit1 * (D + 2);
+    float M;
+    const float L = merge_partials<D, kCombineThreads, 12>(pp, nsplit1, D + 2, false, red, oa, nullptr, grp, &M);
+    if (tid < D) {
+        const float oc = oa[tid] / L;
+        o32[(size_t)bh * D + tid] = oc;
+        if (o) o[(size_t)bh * D + tid] = f32_to_bf16_rne(oc);
+    }
+    if (tid == 0) lse[bh] = M + __logf(L);
 }
 
 DensePlan dense_plan(int B, int H, int n_body) {
@@ -339,12 +445,14 @@ int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, float s
     unsigned* counters = reinterpret_cast<unsigned*>(ws);
     float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_counter_bytes(ca.B, ca.H));
     dim3 grid(pl.nsplit + 1, ca.H, ca.B);
-    if (D == 128)
-        dense_split_kernel<128><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, counters, pl.nsplit, pl.spb,
-                                                      o, o32, lse);
-    else
-        dense_split_kernel<64><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, counters, pl.nsplit, pl.spb,
-                                                     o, o32, lse);
+    (void)counters;
+    if (D == 128) {
+        dense_split_kernel<128><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
+        dense_combine_kernel<128><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit + 1, o, o32, lse);
+    } else {
+        dense_split_kernel<64><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
+        dense_combine_kernel<64><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit + 1, o, o32, lse);
+    }
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
 }
 

@@ -244,6 +244,29 @@ __global__ __launch_bounds__(64) void append_tail_kernel(int H, int D, int pos0,
     }
 }
 
+// every loop at once: k, v [loops][B][H][n_rows][D]; grid.z = B * loops
+__global__ __launch_bounds__(64) void append_tail_all_kernel(CacheArg ca, int D, int pos0, int n_rows,
+                                                             const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v) {
+    const int i = blockIdx.x, h = blockIdx.y;
+    const int b = blockIdx.z % ca.B, r = blockIdx.z / ca.B;
+    const size_t src = ((((size_t)r * ca.B + b) * ca.H + h) * n_rows + i) * D;
+    const size_t dst = ((size_t)((size_t)b * ca.H + h) * kTail + ((pos0 + i) % kTail)) * D;
+    uint16_t* tk = const_cast<uint16_t*>(ca.tail_k[r]);
+    uint16_t* tv = const_cast<uint16_t*>(ca.tail_v[r]);
+    for (int c = threadIdx.x; c < D; c += 64) {
+        tk[dst + c] = k[src + c];
+        tv[dst + c] = v[src + c];
+    }
+}
+
+int launch_append_all(const CacheArg& ca, int D, int pos0, int n_rows, const uint16_t* k, const uint16_t* v,
+                      hipStream_t st) {
+    dim3 grid(n_rows, ca.H, ca.B * ca.nplanes);
+    append_tail_all_kernel<<<grid, 64, 0, st>>>(ca, D, pos0, n_rows, k, v);
+    return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
+}
+
 int launch_encode(const CacheArg& ca, int D, int loop, int pos0, int n_pos, const int32_t* act_pos,
                   const int32_t* n_act, int ld_act, const uint16_t* ksrc, const uint16_t* vsrc, int ld_src,
                   hipStream_t st) {

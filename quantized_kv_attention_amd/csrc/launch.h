@@ -10,6 +10,8 @@ int launch_encode(const CacheArg& ca, int D, int loop, int pos0, int n_pos, cons
                   hipStream_t st);
 int launch_append(int B, int H, int D, int pos0, int n_rows, const uint16_t* k, const uint16_t* v, uint16_t* tk,
                   uint16_t* tv, hipStream_t st);
+int launch_append_all(const CacheArg& ca, int D, int pos0, int n_rows, const uint16_t* k, const uint16_t* v,
+                      hipStream_t st);
 
 // split-KV plan of the dense reader: blocks per split and number of body splits
 struct DensePlan {
