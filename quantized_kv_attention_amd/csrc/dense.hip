@@ -103,7 +103,7 @@ __device__ __forceinline__ void vpass_block(const uint8_t* bp, int prt, int rsub
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                           float sm, float* __restrict__ scores, int ld,
                                                           float* __restrict__ part, int nsplit, int spb) {
     constexpr int LPR = Block<D>::kLpr, RPI = Block<D>::kRpi, NLD = 64 / RPI;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop,
 
     for (int c = tid; c < D; c += 256) qsh[c] = bf16_to_f32(q[(size_t)bh * D + c]) * sm;
     __syncthreads();
-    float* out = part + ((size_t)bh * (nsplit + 1) + s) * (D + 2);
+    float* out = part + ((size_t)bh * nsplit + s) * (D + 2);
     float* srow = scores + (size_t)bh * ld;
 
     float acc[32];
@@ -131,70 +131,14 @@ __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop,
     float vb = 0.f;
     float mx, lsum;
 
-    if (s == nsplit) {
-        // ---- BF16 tail: positions [n_body, n_ctx) at ring slots t % 128 ----
-        const int T = ca.n_ctx - ca.n_body;
-        const uint16_t* tk = ca.tail_k[loop - 1] + (size_t)bh * kTail * D;
-        const uint16_t* tv = ca.tail_v[loop - 1] + (size_t)bh * kTail * D;
-        float qv[32];
-#pragma unroll
-        for (int k = 0; k < 32; ++k) qv[k] = qsh[32 * prt + k];
-        for (int i0 = wave * RPI; i0 < T; i0 += 4 * RPI) {
-            const int i = i0 + rsub;
-            float v = 0.f;
-            if (i < T) {
-                const uint16_t* kr = tk + (size_t)((ca.n_body + i) % kTail) * D + 32 * prt;
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4) {
-                    const uint4 w = *reinterpret_cast<const uint4*>(kr + 8 * k4);
-                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        v = fmaf(qv[8 * k4 + 2 * e], bf16_to_f32(ws[e] & 0xFFFFu), v);
-                        v = fmaf(qv[8 * k4 + 2 * e + 1], bf16_to_f32(ws[e] >> 16), v);
-                    }
-                }
-            }
-            v = group_sum<LPR>(v);
-            if (prt == 0 && i < T) logit[i] = v;
-        }
-        __syncthreads();
-        float lm = -__builtin_huge_valf();
-        for (int i = tid; i < T; i += 256) {
-            srow[ca.n_body + i] = logit[i];
-            lm = fmaxf(lm, logit[i]);
-        }
-        mx = block_reduce_max(lm, red);
-        float ls = 0.f;
-        for (int i = tid; i < T; i += 256) {
-            const float pv = __expf(logit[i] - mx);
-            logit[i] = pv;
-            ls += pv;
-        }
-        lsum = block_reduce_sum(ls, red);
-        for (int i0 = wave * RPI; i0 < T; i0 += 4 * RPI) {
-            const int i = i0 + rsub;
-            if (i < T) {
-                const float pw = logit[i];
-                const uint16_t* vr = tv + (size_t)((ca.n_body + i) % kTail) * D + 32 * prt;
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4) {
-                    const uint4 w = *reinterpret_cast<const uint4*>(vr + 8 * k4);
-                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc[8 * k4 + 2 * e] = fmaf(pw, bf16_to_f32(ws[e] & 0xFFFFu), acc[8 * k4 + 2 * e]);
-                        acc[8 * k4 + 2 * e + 1] = fmaf(pw, bf16_to_f32(ws[e] >> 16), acc[8 * k4 + 2 * e + 1]);
-                    }
-                }
-            }
-        }
-    } else {
-        // ---- body split: blocks [blk0, blk1) ----
+    {
+        // ---- body split: blocks [blk0, blk1); the last split also takes the BF16 tail ----
         const int nblk = ca.n_body / 64;
         const int blk0 = s * spb, blk1 = min(blk0 + spb, nblk);
-        const int nb = blk1 - blk0;
+        const int nb = max(0, blk1 - blk0);
         const int j0 = blk0 * 64, L = nb * 64;
+        const bool has_tail = (s == nsplit - 1);
+        const int T = has_tail ? ca.n_ctx - ca.n_body : 0;  // tail rows land in logit[L + i]
         const int nstart = ca.cap_ctx / 64 + 1;
         {
         // leading dense planes are read block by block together; their folded queries are
@@ -273,14 +217,40 @@ __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop,
             }
             __syncthreads();
         }
+        if (has_tail) {
+            const uint16_t* tk = ca.tail_k[loop - 1] + (size_t)bh * kTail * D;
+            float qv[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k) qv[k] = qsh[32 * prt + k];
+            for (int i0 = wave * RPI; i0 < T; i0 += 4 * RPI) {
+                const int i = i0 + rsub;
+                float v = 0.f;
+                if (i < T) {
+                    const uint16_t* kr = tk + (size_t)((ca.n_body + i) % kTail) * D + 32 * prt;
+#pragma unroll
+                    for (int k4 = 0; k4 < 4; ++k4) {
+                        const uint4 w = *reinterpret_cast<const uint4*>(kr + 8 * k4);
+                        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v = fmaf(qv[8 * k4 + 2 * e], bf16_to_f32(ws[e] & 0xFFFFu), v);
+                            v = fmaf(qv[8 * k4 + 2 * e + 1], bf16_to_f32(ws[e] >> 16), v);
+                        }
+                    }
+                }
+                v = group_sum<LPR>(v);
+                if (prt == 0 && i < T) logit[L + i] = v;
+            }
+            __syncthreads();
+        }
         float lm = -__builtin_huge_valf();
-        for (int i = tid; i < L; i += 256) {
-            srow[j0 + i] = logit[i];
+        for (int i = tid; i < L + T; i += 256) {
+            srow[j0 + i] = logit[i];   // the tail rows follow the split's body rows (j0 + L == n_body)
             lm = fmaxf(lm, logit[i]);
         }
         mx = block_reduce_max(lm, red);
         float ls = 0.f;
-        for (int i = tid; i < L; i += 256) {
+        for (int i = tid; i < L + T; i += 256) {
             const float pv = __expf(logit[i] - mx);
             logit[i] = pv;
             ls += pv;
@@ -345,6 +315,26 @@ __global__ __launch_bounds__(256) void dense_split_kernel(CacheArg ca, int loop,
             }
         }
         }  // general path
+        if (has_tail) {
+            const uint16_t* tv = ca.tail_v[loop - 1] + (size_t)bh * kTail * D;
+            for (int i0 = wave * RPI; i0 < T; i0 += 4 * RPI) {
+                const int i = i0 + rsub;
+                if (i < T) {
+                    const float pw = logit[L + i];
+                    const uint16_t* vr = tv + (size_t)((ca.n_body + i) % kTail) * D + 32 * prt;
+#pragma unroll
+                    for (int k4 = 0; k4 < 4; ++k4) {
+                        const uint4 w = *reinterpret_cast<const uint4*>(vr + 8 * k4);
+                        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            acc[8 * k4 + 2 * e] = fmaf(pw, bf16_to_f32(ws[e] & 0xFFFFu), acc[8 * k4 + 2 * e]);
+                            acc[8 * k4 + 2 * e + 1] = fmaf(pw, bf16_to_f32(ws[e] >> 16), acc[8 * k4 + 2 * e + 1]);
+                        }
+                    }
+                }
+            }
+        }
     }
 
     // reduce the per-lane accumulators over the rows of the wave, then over waves
@@ -419,13 +409,16 @@ DensePlan dense_plan(int B, int H, int n_body) {
     DensePlan pl;
     if (nblk == 0) {
         pl.spb = 1;
-        pl.nsplit = 0;
+        pl.nsplit = 1;  // the tail alone
         return pl;
     }
-    // aim for about 1024 body workgroups, 4..16 blocks each
-    long target = 1024;
-    int spb = (int)(((long)nblk * B * H + target - 1) / target);
-    spb = spb < 4 ? 4 : (spb > kMaxSpb ? kMaxSpb : spb);
+    // One round of workgroups: 4 resident per CU x 256 CUs.  Fewer blocks per split than
+    // that would leave a second round; more than kMaxSpb - 2 leaves no LDS for the tail.
+    const long slots = 1024;
+    long per_bh = slots / ((long)B * H);
+    if (per_bh < 1) per_bh = 1;
+    int spb = (int)((nblk + per_bh - 1) / per_bh);
+    spb = spb < 4 ? 4 : (spb > kMaxSpb - 2 ? kMaxSpb - 2 : spb);  // leave room for 127 tail rows
     pl.spb = spb;
     pl.nsplit = (nblk + spb - 1) / spb;
     return pl;
@@ -436,7 +429,7 @@ size_t ws_counter_bytes(int B, int H) { return (((size_t)B * H * sizeof(unsigned
 
 size_t dense_ws_bytes(int B, int H, int D, int n_body) {
     const DensePlan pl = dense_plan(B, H, n_body);
-    return ws_counter_bytes(B, H) + (size_t)B * H * (pl.nsplit + 1) * (D + 2) * sizeof(float);
+    return ws_counter_bytes(B, H) + (size_t)B * H * pl.nsplit * (D + 2) * sizeof(float);
 }
 
 int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, uint16_t* o, float* o32,
@@ -444,14 +437,14 @@ int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, float s
     const DensePlan pl = dense_plan(ca.B, ca.H, ca.n_body);
     unsigned* counters = reinterpret_cast<unsigned*>(ws);
     float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_counter_bytes(ca.B, ca.H));
-    dim3 grid(pl.nsplit + 1, ca.H, ca.B);
+    dim3 grid(pl.nsplit, ca.H, ca.B);
     (void)counters;
     if (D == 128) {
         dense_split_kernel<128><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
-        dense_combine_kernel<128><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit + 1, o, o32, lse);
+        dense_combine_kernel<128><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit, o, o32, lse);
     } else {
         dense_split_kernel<64><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
-        dense_combine_kernel<64><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit + 1, o, o32, lse);
+        dense_combine_kernel<64><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit, o, o32, lse);
     }
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
 }
