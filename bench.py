@@ -25,6 +25,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+COPY_BYTES = 1 << 30            # the calibration copy reads and writes this many bytes per launch
+COPY_REPS = 8
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dense_split_kernel_ctx32k_traffic.txt")
+DENSE_KERNELS = ("dense_split_kernel", "dense_combine_kernel")
 
 
 def parse():
@@ -34,17 +38,31 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--workload", default="ctx32k")
-    ap.add_argument("--cpu-heads", type=int, default=4)
-    ap.add_argument("--cpu-steps", type=int, default=96)
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="the oracle baseline runs decode steps until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=4, help="timed launches per layer of the dominant kernel")
     ap.add_argument("--profile-dense", action="store_true",
                     help="only launch the loop-2 dense reader (for counter runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain elementwise copy of 1 GiB (reference for the byte counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write a per-kernel table of the rocprofv3 kernel trace under DIR to --out")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of --profile-dense and of "
+                         "--copy-calibration): write the calibrated HBM bytes of the dense reader to --out")
+    ap.add_argument("--out", help="output file of the summaries")
+    ap.add_argument("--cmd", default="", help="command line recorded in a summary")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        return summarize_trace(args)
+    if args.summarize_traffic:
+        return summarize_traffic(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -60,6 +78,14 @@ def main():
     from quantized_kv_attention_amd import synth
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(COPY_REPS):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {COPY_REPS} x neg over {COPY_BYTES} B", file=sys.stderr, flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     L = args.layers
     n = w.n
@@ -231,19 +257,11 @@ def main():
     print(f"[bench] loop-2 dense reader: {dense2_bytes / 1e6:.1f} MB/launch, mean {dense2_us:.2f} us "
           f"(median {dense2_med:.2f}) -> {achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "dense_loop2_ctx32k_traffic.json")
-    if os.path.exists(tfile):
-        try:
-            t = json.load(open(tfile))
-            if t.get("kernel_source_hash") == _dense_source_hash():
-                traffic = t.get("hbm_bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = read_traffic()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_heads, args.cpu_steps)
+        cpu = cpu_baseline(w, args.cpu_heads, args.cpu_seconds)
 
     out = {
         "metric": "decode-attn us/step & achieved HBM GB/s (% peak), 32K ctx, 4 loops, 1 GPU",
@@ -267,7 +285,7 @@ def main():
         "pct_peak_step": round(100 * gbps_step / HBM_PEAK_GBPS, 2),
         "bytes_per_layer_step": int(step_bytes),
         "bytes_per_loop": [int(x) for x in loop_bytes],
-        "roofline": {"bound": "hbm", "kernel": "dense_split_kernel<128> (loop 2: base + loop-2 residual plane)",
+        "roofline": {"bound": "hbm", "kernel": "dense_split_kernel<128, 2> + dense_combine_kernel<128> (one loop-2 reader call: base + loop-2 residual plane)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": int(dense2_bytes), "mean_launch_us": round(dense2_us, 3)},
@@ -284,9 +302,106 @@ def _dense_source_hash():
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(w, heads, steps):
-    """The fp64 oracle on `heads` heads of the same workload, one decode step (all loops)
-    from the encoded cache per query, scaled to all heads of one layer."""
+def read_traffic():
+    """HBM bytes per launch of the dense reader from the committed counter summary, or None
+    when the summary is missing or was taken on another version of the kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith((" ", "#", "|")):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_hash") != _dense_source_hash():
+        return None
+    try:
+        return int(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _rocprof_db(d):
+    import glob
+    dbs = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+    import sqlite3
+    return sqlite3.connect(dbs[0])
+
+
+def _short(name):
+    """Kernel name without its trailing parameter list."""
+    name = name.strip()
+    if name.endswith(")"):
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(name[i], 0)
+            if depth == 0:
+                return name[:i].strip()
+    return name
+
+
+def summarize_trace(args):
+    """Per-kernel launch count and durations of a `rocprofv3 --kernel-trace --stats` run."""
+    con = _rocprof_db(args.summarize_trace)
+    rows = list(con.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+                            "from kernels group by name order by sum(duration) desc"))
+    tot = sum(r[5] for r in rows) or 1
+    lines = [f"# rocprofv3 kernel trace summary", f"command: {args.cmd}", "",
+             "| kernel | launches | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for name, cnt, avg, mn, mx, sm in rows:
+        lines.append(f"| {_short(name)[:90]} | {cnt} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | "
+                     f"{100 * sm / tot:.1f}% |")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _counter_per_dispatch(d, counter, names):
+    """Mean value of `counter` per dispatch of each kernel whose name contains one of `names`."""
+    con = _rocprof_db(d)
+    vals = {}
+    for name, cn, cv in con.execute("select name, counter_name, counter_value from pmc_events"):
+        if cn != counter:
+            continue
+        for k in names:
+            if k in name:
+                vals.setdefault(k, []).append(float(cv))
+    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+
+def summarize_traffic(args):
+    """Calibrated HBM bytes per launch of the dense reader (split + combine kernels).
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same counters read
+    for a plain elementwise copy that reads and writes COPY_BYTES each."""
+    fdir, wdir, cfdir, cwdir = args.summarize_traffic
+    cf = _counter_per_dispatch(cfdir, "FETCH_SIZE", ("neg",)).get("neg")
+    cw = _counter_per_dispatch(cwdir, "WRITE_SIZE", ("neg",)).get("neg")
+    if not cf or not cw:
+        raise SystemExit("copy calibration dispatches not found")
+    f_fac = COPY_BYTES / (cf[0] * 1024.0)
+    w_fac = COPY_BYTES / (cw[0] * 1024.0)
+    fe = _counter_per_dispatch(fdir, "FETCH_SIZE", DENSE_KERNELS)
+    wr = _counter_per_dispatch(wdir, "WRITE_SIZE", DENSE_KERNELS)
+    rd = sum(fe[k][0] for k in fe) * 1024.0 * f_fac
+    wt = sum(wr[k][0] for k in wr) * 1024.0 * w_fac
+    lines = ["# HBM traffic of the loop-2 dense reader, 32K context (16 heads x 128, one launch = split + combine)",
+             f"command: {args.cmd}", "",
+             "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | dispatches |", "|---|---|---|---|"]
+    for k in DENSE_KERNELS:
+        lines.append(f"| {k} | {fe.get(k, (0, 0))[0]:.1f} | {wr.get(k, (0, 0))[0]:.1f} | {fe.get(k, (0, 0))[1]} |")
+    lines += ["", f"| copy of {COPY_BYTES} B | {cf[0]:.1f} | {cw[0]:.1f} | {cf[1]} |", "",
+              f"fetch_factor: {f_fac:.4f}", f"write_factor: {w_fac:.4f}",
+              f"read_bytes_per_launch: {int(rd)}", f"write_bytes_per_launch: {int(wt)}",
+              f"hbm_bytes_per_launch: {int(rd + wt)}", f"kernel_source_hash: {_dense_source_hash()}"]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cpu_baseline(w, heads, seconds):
+    """The fp64 oracle on `heads` heads of the same workload: decode steps (every loop, from
+    the encoded cache) until `seconds` of wall time have passed, scaled to all heads of one
+    layer.  The cache build is not timed."""
     import numpy as np
 
     import oracle as orc
@@ -300,16 +415,19 @@ def cpu_baseline(w, heads, steps):
     kn, vn = synth.gen_new_token(w, 1000, heads=hs)
     oc.append(kn, vn)
     k = w.k_cols(oc.n)
-    threads = min(len(hs) * w.B, os.cpu_count() or 1)
-    qs = [synth.gen_queries(w, 2000 + s, heads=hs) for s in range(steps)]
+    threads = max(1, min(len(hs) * w.B, os.cpu_count() or 1, 16))
+    steps = 0
     t0 = time.perf_counter()
-    for s in range(steps):
-        oc.step(qs[s], w.n_dense, k, threads=threads)
-    dt = time.perf_counter() - t0
+    while True:
+        oc.step(synth.gen_queries(w, 2000 + steps, heads=hs), w.n_dense, k, threads=threads)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds or steps >= 100000:
+            break
     per_step_us = dt / steps * 1e6 * (w.H / len(hs))
     return {"value": round(per_step_us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
             "sample": f"{len(hs)} of {w.H} heads x {steps} decode steps (all {w.R} loops, context {oc.n}), "
-                      f"{dt:.1f} s wall, scaled to {w.H} heads"}
+                      f"{dt:.1f} s wall on {threads} threads" + (f", scaled to {w.H} heads" if len(hs) < w.H else "")}
 
 
 if __name__ == "__main__":

@@ -10,13 +10,12 @@
 // Each workgroup (4 waves) owns a contiguous range of 64-position blocks: pass 1 streams
 // the K codes of every plane into LDS logits, then a local softmax, pass 2 streams the V
 // codes; partial (max, sum, o) go to the workspace and a second kernel merges the splits
-// in a fixed order.  One extra workgroup per (sequence, head) reads the BF16 tail.
+// in a fixed order.  The last split of each (sequence, head) also reads the BF16 tail.
 #include "launch.h"
 
 namespace qkv {
 
 constexpr int kMaxSpb = 16;  // 64-position blocks per split, at most
-constexpr int kMaxPre = 2;   // leading dense planes whose folded queries are prepared per split
 
 __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -102,7 +101,10 @@ __device__ __forceinline__ void vpass_block(const uint8_t* bp, int prt, int rsub
     }
 }
 
-template <int D>
+// NPRE (1 or 2): leading dense planes whose blocks are read together, with their folded
+// queries prepared once per split; later planes (sparse, or dense beyond NPRE) follow one
+// by one.
+template <int D, int NPRE>
 __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                           float sm, float* __restrict__ scores, int ld,
                                                           float* __restrict__ part, int nsplit, int spb) {
@@ -114,8 +116,8 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
 
     __shared__ float qsh[D];
     __shared__ float logit[kMaxSpb * 64];
-    __shared__ float qpre[kMaxPre][kMaxSpb][D];
-    __shared__ float bpre[kMaxPre][kMaxSpb];
+    __shared__ float qpre[NPRE][kMaxSpb][D];
+    __shared__ float bpre[NPRE][kMaxSpb];
     __shared__ float qps[4][D];
     __shared__ float red[4];
     __shared__ float ored[4][D];
@@ -143,8 +145,7 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
         {
         // leading dense planes are read block by block together; their folded queries are
         // prepared once per split (one wave per (plane, block))
-        int npre = 0;
-        while (npre < kMaxPre && npre < loop && ca.p[npre].dense) ++npre;
+        constexpr int npre = NPRE;
         for (int i = wave; i < npre * nb; i += 4) {
             const int p = i / nb, bb = i % nb;
             const float bias = fold_query<D>(block_ptr<D>(ca.p[p], ca.H, b, h, blk0 + bb), qsh, qpre[p][bb], lane);
@@ -155,9 +156,9 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
         // K pass, prepared planes: logits of every row of the block summed over the planes
         for (int blk = blk0 + wave; blk < blk1; blk += 4) {
             const int bb = blk - blk0;
-            uint4 w[kMaxPre][NLD];
+            uint4 w[NPRE][NLD];
 #pragma unroll
-            for (int p = 0; p < kMaxPre; ++p) {
+            for (int p = 0; p < NPRE; ++p) {
                 if (p < npre) {
                     const uint8_t* bp = block_ptr<D>(ca.p[p], ca.H, b, h, blk);
 #pragma unroll
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
             for (int it = 0; it < NLD; ++it) lg[it] = 0.f;
             float bias = 0.f;
 #pragma unroll
-            for (int p = 0; p < kMaxPre; ++p) {
+            for (int p = 0; p < NPRE; ++p) {
                 if (p < npre) {
                     float qp[32];
 #pragma unroll
@@ -260,10 +261,10 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
         // V pass, prepared planes: every plane's codes of the block loaded together
         for (int blk = blk0 + wave; blk < blk1; blk += 4) {
             const int bb = blk - blk0;
-            uint4 w[kMaxPre][NLD];
-            float2 m[kMaxPre][NLD];
+            uint4 w[NPRE][NLD];
+            float2 m[NPRE][NLD];
 #pragma unroll
-            for (int p = 0; p < kMaxPre; ++p) {
+            for (int p = 0; p < NPRE; ++p) {
                 if (p < npre) {
                     const uint8_t* bp = block_ptr<D>(ca.p[p], ca.H, b, h, blk);
 #pragma unroll
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
             for (int it = 0; it < NLD; ++it) {
                 const float pw = logit[bb * 64 + rsub + RPI * it];
 #pragma unroll
-                for (int p = 0; p < kMaxPre; ++p) {
+                for (int p = 0; p < NPRE; ++p) {
                     if (p < npre) {
                         vb = fmaf(pw, m[p][it].y, vb);
                         axpy32_fp8(w[p][it], pw * m[p][it].x * kFp8CodeScale, acc);
@@ -439,11 +440,19 @@ int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, float s
     float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_counter_bytes(ca.B, ca.H));
     dim3 grid(pl.nsplit, ca.H, ca.B);
     (void)counters;
+    // plane 1 (the base) is always dense; plane 2 joins it when it is dense too
+    const bool two = loop >= 2 && ca.p[1].dense;
     if (D == 128) {
-        dense_split_kernel<128><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
+        if (two)
+            dense_split_kernel<128, 2><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
+        else
+            dense_split_kernel<128, 1><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
         dense_combine_kernel<128><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit, o, o32, lse);
     } else {
-        dense_split_kernel<64><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
+        if (two)
+            dense_split_kernel<64, 2><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
+        else
+            dense_split_kernel<64, 1><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
         dense_combine_kernel<64><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit, o, o32, lse);
     }
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
