@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="the oracle baseline runs decode steps until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--inline-select", action="store_true",
+                    help="run each column selection on the main stream instead of the side stream")
     ap.add_argument("--kernel-reps", type=int, default=4, help="timed launches per layer of the dominant kernel")
     ap.add_argument("--profile-dense", action="store_true",
                     help="only launch the loop-2 dense reader (for counter runs)")
@@ -126,6 +128,8 @@ def main():
     print(f"[bench] {L} layer caches of {layers[0]['c'].nbytes() / 1e6:.1f} MB ready in {setup_s:.1f}s "
           f"(n={n_step}, k={k})", file=sys.stderr, flush=True)
 
+    side = None if args.inline_select else qcache.SideSelect()
+
     def step(with_flush):
         for ly in layers:
             c = ly["c"]
@@ -139,7 +143,7 @@ def main():
             qkv.kv_append_tail(c, 0, n, ly["kn"], ly["vn"])  # every loop in one launch
         for loop in range(1, w.R + 1):
             for ly in layers:
-                qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k)
+                qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k, side=side)
 
     def dense2():
         for ly in layers:
@@ -280,6 +284,7 @@ def main():
                                f"token retention {w.rho}, {int(w.k_frac * 100)}% key columns in loops "
                                f"{w.n_dense + 1}-{w.R}, INT4 g64 + fp32 scale/zero, 64-token BF16 tail",
                    "layers_rotated": L, "k_columns": k, "step": "append + amortised 64-row flush + R-loop attention",
+                   "selection": "inline" if args.inline_select else "side stream, issued after the previous loop",
                    "value_is": "microseconds per decode step of one layer"},
         "hbm_GBps_step": round(gbps_step, 1),
         "pct_peak_step": round(100 * gbps_step / HBM_PEAK_GBPS, 2),

@@ -112,8 +112,8 @@ int qkv_body_len(int n_ctx);
 /*
  * Workspace bytes that attn_decode_dense, attn_decode_sparse and select_columns need for
  * caches of this shape with up to max_ctx positions and up to max_k selected columns.
- * The workspace is device memory owned by the caller; it must be zero-filled once
- * before its first use and is left zero-filled by every call.
+ * The workspace is device memory owned by the caller; it needs no initialisation and
+ * holds nothing between calls (calls that use one workspace must not overlap).
  */
 size_t qkv_workspace_bytes(int batch, int heads, int head_dim, int max_ctx, int max_k);
 

@@ -180,6 +180,7 @@ class DecodeBuffers:
         self.B, self.H = B, H
         nbytes = workspace_bytes(B, H, d, cache.cap, self.max_k)
         self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.pending = {}   # loop -> (k, event) of a selection issued on a side stream
 
     def selection(self, loop: int, k: int):
         """Views (idx, p_sel, mass) of loop `loop`'s selection of k columns."""
@@ -194,22 +195,56 @@ def k_columns(frac: float, n: int) -> int:
     return min(n, int(math.ceil(frac * n)))
 
 
+class SideSelect:
+    """Second stream (default priority) for the column selections of sparse loops.
+
+    Loop r+1's selection reads only loop r's scores and lse, so it can start as soon as
+    loop r of the same layer is done, beside whatever the main stream runs next (in a
+    looped model: loop r of the following layers).  The sparse loop waits for it."""
+
+    def __init__(self):
+        self.stream = torch.cuda.Stream()
+
+    def issue(self, cache, bufs, loop, k, main):
+        ev = torch.cuda.Event()
+        ev.record(main)
+        self.stream.wait_event(ev)
+        idx, ps, mass = bufs.selection(loop, k)
+        select_columns(bufs.scores, bufs.lse, cache.n_ctx, k, idx, ps, mass, None, self.stream)
+        done = torch.cuda.Event()
+        done.record(self.stream)
+        bufs.pending[loop] = (k, done)
+
+
 def decode_loop(cache: LayerCache, bufs: DecodeBuffers, loop: int, q, n_dense: int, k: int, sm: float = 1.0,
-                stream=None):
-    """Attention of loop `loop` (1-based) for query q [B, H, d] bf16."""
+                stream=None, side: SideSelect | None = None):
+    """Attention of loop `loop` (1-based) for query q [B, H, d] bf16.
+
+    With `side`, the selection of the next loop is issued on the side stream as soon as
+    this loop's scores are written, and a sparse loop consumes the selection issued for it."""
     r = loop - 1
+    main = torch.cuda.current_stream() if stream is None else stream
     if loop <= n_dense:
-        attn_decode_dense(cache, loop, q, sm, bufs.o[r], bufs.o_f32[r], bufs.scores, bufs.lse, bufs.ws, stream)
-        return
-    n = cache.n_ctx
-    assert k <= bufs.max_k
-    idx, ps, mass = bufs.selection(loop, k)
-    select_columns(bufs.scores, bufs.lse, n, k, idx, ps, mass, None, stream)
-    attn_decode_sparse(cache, loop, q, sm, idx, ps, mass, k, bufs.o_f32[r - 1], bufs.lse, bufs.scores,
-                       bufs.o[r], bufs.o_f32[r], bufs.ws, stream)
+        attn_decode_dense(cache, loop, q, sm, bufs.o[r], bufs.o_f32[r], bufs.scores, bufs.lse, bufs.ws, main)
+    else:
+        n = cache.n_ctx
+        assert k <= bufs.max_k
+        idx, ps, mass = bufs.selection(loop, k)
+        pend = bufs.pending.pop(loop, None)
+        if pend is not None and pend[0] == k:
+            main.wait_event(pend[1])
+        else:
+            if pend is not None:
+                main.wait_event(pend[1])   # a stale selection must finish before it is overwritten
+            select_columns(bufs.scores, bufs.lse, n, k, idx, ps, mass, None, main)
+        attn_decode_sparse(cache, loop, q, sm, idx, ps, mass, k, bufs.o_f32[r - 1], bufs.lse, bufs.scores,
+                           bufs.o[r], bufs.o_f32[r], bufs.ws, main)
+    if side is not None and n_dense <= loop < cache.R:
+        side.issue(cache, bufs, loop + 1, k, main)
 
 
-def decode_step(cache: LayerCache, bufs: DecodeBuffers, q, n_dense: int, k: int, sm: float = 1.0, stream=None):
+def decode_step(cache: LayerCache, bufs: DecodeBuffers, q, n_dense: int, k: int, sm: float = 1.0, stream=None,
+                side: SideSelect | None = None):
     """All loops of one decode step of one layer; q[r] bf16 [B, H, d]."""
     for loop in range(1, cache.R + 1):
-        decode_loop(cache, bufs, loop, q[loop - 1], n_dense, k, sm, stream)
+        decode_loop(cache, bufs, loop, q[loop - 1], n_dense, k, sm, stream, side)

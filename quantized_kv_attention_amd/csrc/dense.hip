@@ -425,21 +425,17 @@ DensePlan dense_plan(int B, int H, int n_body) {
     return pl;
 }
 
-// workspace: per-(sequence, head) counters first, then the split partials
-size_t ws_counter_bytes(int B, int H) { return (((size_t)B * H * sizeof(unsigned)) + 255) & ~(size_t)255; }
-
+// workspace: the split partials [B][H][nsplit][2 + D]
 size_t dense_ws_bytes(int B, int H, int D, int n_body) {
     const DensePlan pl = dense_plan(B, H, n_body);
-    return ws_counter_bytes(B, H) + (size_t)B * H * pl.nsplit * (D + 2) * sizeof(float);
+    return (size_t)B * H * pl.nsplit * (D + 2) * sizeof(float);
 }
 
 int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, uint16_t* o, float* o32,
                  float* scores, int ld, float* lse, void* ws, hipStream_t st) {
     const DensePlan pl = dense_plan(ca.B, ca.H, ca.n_body);
-    unsigned* counters = reinterpret_cast<unsigned*>(ws);
-    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_counter_bytes(ca.B, ca.H));
+    float* part = static_cast<float*>(ws);
     dim3 grid(pl.nsplit, ca.H, ca.B);
-    (void)counters;
     // plane 1 (the base) is always dense; plane 2 joins it when it is dense too
     const bool two = loop >= 2 && ca.p[1].dense;
     if (D == 128) {

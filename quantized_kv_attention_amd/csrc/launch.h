@@ -19,7 +19,6 @@ struct DensePlan {
     int nsplit;
 };
 DensePlan dense_plan(int B, int H, int n_body);
-size_t ws_counter_bytes(int B, int H);
 size_t dense_ws_bytes(int B, int H, int D, int n_body);
 int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, uint16_t* o, float* o32,
                  float* scores, int ld, float* lse, void* ws, hipStream_t st);

@@ -247,7 +247,7 @@ __global__ __launch_bounds__(D) void sparse_copy_kernel(const float* o_prev, uin
 
 size_t sparse_ws_bytes(int B, int H, int D, int k) {
     const int nchunk = (k + kChunk - 1) / kChunk;
-    return ws_counter_bytes(B, H) + (size_t)B * H * nchunk * (2 + 2 * D) * sizeof(float);
+    return (size_t)B * H * nchunk * (2 + 2 * D) * sizeof(float);
 }
 
 int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, const int32_t* idx,
@@ -261,7 +261,7 @@ int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, float 
             sparse_copy_kernel<64><<<ca.B * ca.H, 64, 0, st>>>(o_prev, o, o32);
         return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
     }
-    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_counter_bytes(ca.B, ca.H));
+    float* part = static_cast<float*>(ws);
     dim3 grid(nchunk, ca.H, ca.B);
     if (D == 128) {
         sparse_chunk_kernel<128><<<grid, 256, 0, st>>>(ca, loop, q, sm, idx, p_sel, k, scores, ld, part);
