@@ -110,7 +110,8 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
                                                           float* __restrict__ part, int nsplit, int spb) {
     constexpr int LPR = Block<D>::kLpr, RPI = Block<D>::kRpi, NLD = 64 / RPI;
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: block addresses stay scalar
     const int prt = lane % LPR, rsub = lane / LPR;
     const int bh = b * ca.H + h;
 
@@ -122,8 +123,31 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
     __shared__ float red[4];
     __shared__ float ored[4][D];
 
+    // ---- body split: blocks [blk0, blk1); the last split also takes the BF16 tail ----
+    const int nblk = ca.n_body / 64;
+    const int blk0 = s * spb, blk1 = min(blk0 + spb, nblk);
+    const int nb = max(0, blk1 - blk0);
+    const int j0 = blk0 * 64, L = nb * 64;
+    const bool has_tail = (s == nsplit - 1);
+    const int T = has_tail ? ca.n_ctx - ca.n_body : 0;  // tail rows land in logit[L + i]
+    const int nstart = ca.cap_ctx / 64 + 1;
+    const int blkA = blk0 + wave;                         // this wave's first block
+    // Prefetches are unconditional (a branch around them makes the compiler wait for them at
+    // the join): a wave without blocks loads a valid block it does not use.
+    const int blkP = max(0, min(blkA, blk1 - 1));
+
+    // Codes of a block of the prepared planes: K codes, V codes + per-row V meta.
+    uint4 wk[NPRE][NLD];
+    auto load_k = [&](int blk) {
+#pragma unroll
+        for (int p = 0; p < NPRE; ++p) {
+            const uint8_t* bp = block_ptr<D>(ca.p[p], ca.H, b, h, blk);
+#pragma unroll
+            for (int it = 0; it < NLD; ++it)
+                wk[p][it] = *reinterpret_cast<const uint4*>(bp + Block<D>::kKc + (rsub + RPI * it) * (D / 2) + prt * 16);
+        }
+    };
     for (int c = tid; c < D; c += 256) qsh[c] = bf16_to_f32(q[(size_t)bh * D + c]) * sm;
-    __syncthreads();
     float* out = part + ((size_t)bh * nsplit + s) * (D + 2);
     float* srow = scores + (size_t)bh * ld;
 
@@ -134,56 +158,73 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
     float mx, lsum;
 
     {
-        // ---- body split: blocks [blk0, blk1); the last split also takes the BF16 tail ----
-        const int nblk = ca.n_body / 64;
-        const int blk0 = s * spb, blk1 = min(blk0 + spb, nblk);
-        const int nb = max(0, blk1 - blk0);
-        const int j0 = blk0 * 64, L = nb * 64;
-        const bool has_tail = (s == nsplit - 1);
-        const int T = has_tail ? ca.n_ctx - ca.n_body : 0;  // tail rows land in logit[L + i]
-        const int nstart = ca.cap_ctx / 64 + 1;
         {
-        // leading dense planes are read block by block together; their folded queries are
-        // prepared once per split (one wave per (plane, block))
+        // Folded queries of the prepared planes, once per split: each wave takes blocks
+        // wave, wave + 4, ... of every prepared plane (the plane index stays a compile-time
+        // constant, so the plane descriptors are scalar loads).  All key scales and zeros
+        // are loaded before any is used.
         constexpr int npre = NPRE;
-        for (int i = wave; i < npre * nb; i += 4) {
-            const int p = i / nb, bb = i % nb;
-            const float bias = fold_query<D>(block_ptr<D>(ca.p[p], ca.H, b, h, blk0 + bb), qsh, qpre[p][bb], lane);
-            if (lane == 0) bpre[p][bb] = bias;
+        constexpr int kFold = (kMaxSpb + 3) / 4;
+        constexpr int CPL = D / 64;  // channels per lane
+        float fs[NPRE][kFold][CPL], fz[NPRE][kFold][CPL];
+#pragma unroll
+        for (int p = 0; p < NPRE; ++p) {
+#pragma unroll
+            for (int u = 0; u < kFold; ++u) {
+                const int bb = wave + 4 * u;
+                if (bb < nb) {
+                    const float* km = reinterpret_cast<const float*>(block_ptr<D>(ca.p[p], ca.H, b, h, blk0 + bb) +
+                                                                     Block<D>::kKm);
+#pragma unroll
+                    for (int cc = 0; cc < CPL; ++cc) {
+                        fs[p][u][cc] = km[lane + 64 * cc];
+                        fz[p][u][cc] = km[D + lane + 64 * cc];
+                    }
+                }
+            }
+        }
+        // the first block's key codes are in flight while the query is folded
+        load_k(blkP);
+        __syncthreads();  // qsh
+#pragma unroll
+        for (int p = 0; p < NPRE; ++p) {
+#pragma unroll
+            for (int u = 0; u < kFold; ++u) {
+                const int bb = wave + 4 * u;
+                if (bb < nb) {
+                    float bias = 0.f;
+#pragma unroll
+                    for (int cc = 0; cc < CPL; ++cc) {
+                        const float qc = qsh[lane + 64 * cc];
+                        qpre[p][bb][lane + 64 * cc] = qc * fs[p][u][cc] * kFp8CodeScale;
+                        bias = fmaf(qc, fz[p][u][cc], bias);
+                    }
+                    bias = wave_sum_dpp(bias);
+                    if (lane == 0) bpre[p][bb] = bias;
+                }
+            }
         }
         __syncthreads();
 
         // K pass, prepared planes: logits of every row of the block summed over the planes
-        for (int blk = blk0 + wave; blk < blk1; blk += 4) {
+        for (int blk = blkA; blk < blk1; blk += 4) {
             const int bb = blk - blk0;
-            uint4 w[NPRE][NLD];
-#pragma unroll
-            for (int p = 0; p < NPRE; ++p) {
-                if (p < npre) {
-                    const uint8_t* bp = block_ptr<D>(ca.p[p], ca.H, b, h, blk);
-#pragma unroll
-                    for (int it = 0; it < NLD; ++it)
-                        w[p][it] = *reinterpret_cast<const uint4*>(bp + Block<D>::kKc + (rsub + RPI * it) * (D / 2) +
-                                                                   prt * 16);
-                }
-            }
+            if (blk != blkA) load_k(blk);
             float lg[NLD];
 #pragma unroll
             for (int it = 0; it < NLD; ++it) lg[it] = 0.f;
             float bias = 0.f;
 #pragma unroll
             for (int p = 0; p < NPRE; ++p) {
-                if (p < npre) {
-                    float qp[32];
+                float qp[32];
 #pragma unroll
-                    for (int k = 0; k < 32; k += 4) {
-                        const float4 t = *reinterpret_cast<const float4*>(&qpre[p][bb][32 * prt + k]);
-                        qp[k] = t.x; qp[k + 1] = t.y; qp[k + 2] = t.z; qp[k + 3] = t.w;
-                    }
-#pragma unroll
-                    for (int it = 0; it < NLD; ++it) lg[it] += dot32_fp8(w[p][it], qp);
-                    bias += bpre[p][bb];
+                for (int k = 0; k < 32; k += 4) {
+                    const float4 t = *reinterpret_cast<const float4*>(&qpre[p][bb][32 * prt + k]);
+                    qp[k] = t.x; qp[k + 1] = t.y; qp[k + 2] = t.z; qp[k + 3] = t.w;
                 }
+#pragma unroll
+                for (int it = 0; it < NLD; ++it) lg[it] += dot32_fp8(wk[p][it], qp);
+                bias += bpre[p][bb];
             }
 #pragma unroll
             for (int it = 0; it < NLD; ++it) {
@@ -244,6 +285,22 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
             }
             __syncthreads();
         }
+        // The first block's value codes are in flight during the softmax.
+        uint4 wv[NPRE][NLD];
+        float2 mv[NPRE][NLD];
+        auto load_v = [&](int blk) {
+#pragma unroll
+            for (int p = 0; p < NPRE; ++p) {
+                const uint8_t* bp = block_ptr<D>(ca.p[p], ca.H, b, h, blk);
+#pragma unroll
+                for (int it = 0; it < NLD; ++it) {
+                    const int row = rsub + RPI * it;
+                    wv[p][it] = *reinterpret_cast<const uint4*>(bp + Block<D>::kVc + row * (D / 2) + prt * 16);
+                    mv[p][it] = *reinterpret_cast<const float2*>(bp + Block<D>::kVm + (row * (D / 64) + (prt >> 1)) * 8);
+                }
+            }
+        };
+        load_v(blkP);
         float lm = -__builtin_huge_valf();
         for (int i = tid; i < L + T; i += 256) {
             srow[j0 + i] = logit[i];   // the tail rows follow the split's body rows (j0 + L == n_body)
@@ -259,32 +316,16 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
         lsum = block_reduce_sum(ls, red);
 
         // V pass, prepared planes: every plane's codes of the block loaded together
-        for (int blk = blk0 + wave; blk < blk1; blk += 4) {
+        for (int blk = blkA; blk < blk1; blk += 4) {
             const int bb = blk - blk0;
-            uint4 w[NPRE][NLD];
-            float2 m[NPRE][NLD];
-#pragma unroll
-            for (int p = 0; p < NPRE; ++p) {
-                if (p < npre) {
-                    const uint8_t* bp = block_ptr<D>(ca.p[p], ca.H, b, h, blk);
-#pragma unroll
-                    for (int it = 0; it < NLD; ++it) {
-                        const int row = rsub + RPI * it;
-                        w[p][it] = *reinterpret_cast<const uint4*>(bp + Block<D>::kVc + row * (D / 2) + prt * 16);
-                        m[p][it] = *reinterpret_cast<const float2*>(bp + Block<D>::kVm +
-                                                                    (row * (D / 64) + (prt >> 1)) * 8);
-                    }
-                }
-            }
+            if (blk != blkA) load_v(blk);
 #pragma unroll
             for (int it = 0; it < NLD; ++it) {
                 const float pw = logit[bb * 64 + rsub + RPI * it];
 #pragma unroll
                 for (int p = 0; p < NPRE; ++p) {
-                    if (p < npre) {
-                        vb = fmaf(pw, m[p][it].y, vb);
-                        axpy32_fp8(w[p][it], pw * m[p][it].x * kFp8CodeScale, acc);
-                    }
+                    vb = fmaf(pw, mv[p][it].y, vb);
+                    axpy32_fp8(wv[p][it], pw * mv[p][it].x * kFp8CodeScale, acc);
                 }
             }
         }
@@ -431,26 +472,26 @@ size_t dense_ws_bytes(int B, int H, int D, int n_body) {
     return (size_t)B * H * pl.nsplit * (D + 2) * sizeof(float);
 }
 
-int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, uint16_t* o, float* o32,
-                 float* scores, int ld, float* lse, void* ws, hipStream_t st) {
+template <int D>
+static void launch_dense_d(const CacheArg& ca, int loop, const uint16_t* q, float sm, uint16_t* o, float* o32,
+                           float* scores, int ld, float* lse, float* part, hipStream_t st) {
     const DensePlan pl = dense_plan(ca.B, ca.H, ca.n_body);
-    float* part = static_cast<float*>(ws);
     dim3 grid(pl.nsplit, ca.H, ca.B);
     // plane 1 (the base) is always dense; plane 2 joins it when it is dense too
-    const bool two = loop >= 2 && ca.p[1].dense;
-    if (D == 128) {
-        if (two)
-            dense_split_kernel<128, 2><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
-        else
-            dense_split_kernel<128, 1><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
-        dense_combine_kernel<128><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit, o, o32, lse);
-    } else {
-        if (two)
-            dense_split_kernel<64, 2><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
-        else
-            dense_split_kernel<64, 1><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
-        dense_combine_kernel<64><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit, o, o32, lse);
-    }
+    if (loop >= 2 && ca.p[1].dense)
+        dense_split_kernel<D, 2><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
+    else
+        dense_split_kernel<D, 1><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
+    dense_combine_kernel<D><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit, o, o32, lse);
+}
+
+int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, uint16_t* o, float* o32,
+                 float* scores, int ld, float* lse, void* ws, hipStream_t st) {
+    float* part = static_cast<float*>(ws);
+    if (D == 128)
+        launch_dense_d<128>(ca, loop, q, sm, o, o32, scores, ld, lse, part, st);
+    else
+        launch_dense_d<64>(ca, loop, q, sm, o, o32, scores, ld, lse, part, st);
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
 }
 

@@ -69,10 +69,11 @@ WORKLOADS = {
 
 
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
-    """fp32 -> bf16 bit pattern, round to nearest even (input formatting only)."""
+    """fp32 -> bf16 bit pattern, round to nearest even (input formatting only; finite
+    inputs: the 32-bit sum cannot carry out of the top bit)."""
     f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = f.view(np.uint32)
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return u.astype(np.uint16)
 
 
@@ -114,13 +115,13 @@ def gen_head_kv(w: Workload, b: int, h: int, act: list, n: int | None = None):
     V[0] = bf16_round_bits(vf)
     for r in range(1, w.R):
         sig = np.float32(w.sigma[r - 1])
-        nk = g.standard_normal((n, w.d), dtype=np.float32)
-        nv = g.standard_normal((n, w.d), dtype=np.float32)
-        a = act[r][b][:, None]
-        kprev = bf16_bits_to_float(K[r - 1])
-        vprev = bf16_bits_to_float(V[r - 1])
-        K[r] = np.where(a, bf16_round_bits(kprev + sig * nk), K[r - 1])
-        V[r] = np.where(a, bf16_round_bits(vprev + sig * nv), V[r - 1])
+        rows = np.nonzero(act[r][b])[0]          # noise is drawn for the active rows only
+        nk = g.standard_normal((rows.size, w.d), dtype=np.float32)
+        nv = g.standard_normal((rows.size, w.d), dtype=np.float32)
+        K[r] = K[r - 1].copy()
+        V[r] = V[r - 1].copy()
+        K[r][rows] = bf16_round_bits(bf16_bits_to_float(K[r - 1][rows]) + sig * nk)
+        V[r][rows] = bf16_round_bits(bf16_bits_to_float(V[r - 1][rows]) + sig * nv)
     return K, V
 
 
@@ -131,12 +132,21 @@ def gen_layer(w: Workload, heads=None, n: int | None = None):
     act = gen_masks(w, n)
     K = [np.zeros((w.B, len(heads), n, w.d), np.uint16) for _ in range(w.R)]
     V = [np.zeros((w.B, len(heads), n, w.d), np.uint16) for _ in range(w.R)]
-    for b in range(w.B):
-        for i, h in enumerate(heads):
-            kh, vh = gen_head_kv(w, b, h, act, n)
-            for r in range(w.R):
-                K[r][b, i] = kh[r]
-                V[r][b, i] = vh[r]
+
+    def one(bi):
+        b, i = bi
+        kh, vh = gen_head_kv(w, b, heads[i], act, n)
+        for r in range(w.R):
+            K[r][b, i] = kh[r]
+            V[r][b, i] = vh[r]
+
+    jobs = [(b, i) for b in range(w.B) for i in range(len(heads))]
+    if len(jobs) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(min(8, len(jobs))) as ex:   # each (b, h) has its own stream
+            list(ex.map(one, jobs))
+    else:
+        one(jobs[0])
     return K, V, act
 
 
