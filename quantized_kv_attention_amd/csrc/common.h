@@ -58,6 +58,13 @@ __device__ __forceinline__ const uint8_t* block_ptr(const PlaneArg& P, int H, in
     return P.data + ((size_t)((size_t)b * H + h) * P.n_blocks + blk) * Block<D>::kBytes;
 }
 
+// Orders one wave's LDS writes before its later LDS reads by other lanes of the same wave.
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
