@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--inline-select", action="store_true",
                     help="run each column selection on the main stream instead of the side stream")
     ap.add_argument("--kernel-reps", type=int, default=4, help="timed launches per layer of the dominant kernel")
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-entry-point measurements")
     ap.add_argument("--profile-dense", action="store_true",
                     help="only launch the loop-2 dense reader (for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -234,10 +235,14 @@ def main():
     # flush of the 64 oldest tail rows: BF16 rows in, the loop's plane rows out, and the
     # rows' chain through planes 1..r-1 re-read to form the residual
     flush_bytes = 0
+    flush_loop_bytes = []
     for r in range(w.R):
+        fb = 0
         for b in range(B):
             stored = 64 if dense[r] else int(act0[r][b, nb:nb + 64].sum())
-            flush_bytes += H * (stored * d * 2 * 2 + bm.plane_bytes(stored, d) * (r + 1))
+            fb += H * bm.encode_bytes(stored, d, r + 1)
+        flush_loop_bytes.append(fb)
+        flush_bytes += fb
     step_bytes += append_bytes + flush_bytes * n_flush / K
     gbps_step = step_bytes / (us_step_layer * 1e-6) / 1e9
 
@@ -262,6 +267,10 @@ def main():
           f"(median {dense2_med:.2f}) -> {achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
     traffic = read_traffic()
+
+    rows_out = None
+    if not args.no_rows:
+        rows_out = measure_rows(w, layers, dense, n, nb, k, loop_bytes, flush_loop_bytes, append_bytes, args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -295,6 +304,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": int(dense2_bytes), "mean_launch_us": round(dense2_us, 3)},
         "cpu_baseline": cpu,
+        "rows": rows_out,
     }
     print(json.dumps(out), flush=True)
 
@@ -305,6 +315,107 @@ def _dense_source_hash():
     for f in ("dense.hip", "common.h"):
         h.update(open(os.path.join(ROOT, "quantized_kv_attention_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def measure_rows(w, layers, dense, n, nb, k, loop_bytes, flush_loop_bytes, append_bytes, args):
+    """Each entry point of the path timed on its own (events around back-to-back calls over
+    the rotated layers), with its algorithmic bytes and the fraction of the HBM peak."""
+    import numpy as np
+    import torch
+
+    import quantized_kv_attention_amd as qkv
+    from quantized_kv_attention_amd import bytes_model as bm
+    from quantized_kv_attention_amd import cache as qcache
+    from quantized_kv_attention_amd import synth
+
+    s = torch.cuda.current_stream()
+
+    def timed(fn, reps=4):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / reps
+
+    def row(us_total, calls, nbytes, bound="hbm"):
+        us = us_total / calls
+        gbps = nbytes / (us * 1e-6) / 1e9
+        return {"us": round(us, 2), "bytes": int(nbytes), "GBps": round(gbps, 1),
+                "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "bound": bound}
+
+    L = len(layers)
+    out = {}
+    kR = lambda r: k  # same key budget in every sparse loop
+
+    # dense loops (every loop the configuration runs densely), selection, sparse loops
+    for loop in range(1, w.R + 1):
+        if loop <= w.n_dense:
+            t = timed(lambda: [qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k)
+                               for ly in layers])
+            out[f"attn_decode_dense loop {loop}"] = row(t, L, loop_bytes[loop - 1])
+        else:
+            sel = lambda ly: qkv.select_columns(ly["b"].scores, ly["b"].lse, n + 1, kR(loop),
+                                                *ly["b"].selection(loop, kR(loop)), None, s)
+            t = timed(lambda: [sel(ly) for ly in layers])
+            out[f"select_columns loop {loop}"] = row(t, L, w.B * w.H * bm.select_bytes(n + 1, k), "latency")
+            def sp(ly):
+                idx, ps, mass = ly["b"].selection(loop, k)
+                qkv.attn_decode_sparse(ly["c"], loop, ly["q"][loop - 1], 1.0, idx, ps, mass, k,
+                                       ly["b"].o_f32[loop - 2], ly["b"].lse, ly["b"].scores, ly["b"].o[loop - 1],
+                                       ly["b"].o_f32[loop - 1], ly["b"].ws, s)
+            t = timed(lambda: [sp(ly) for ly in layers])
+            sel_b = w.B * w.H * bm.select_bytes(n + 1, k)
+            out[f"attn_decode_sparse loop {loop}"] = row(t, L, loop_bytes[loop - 1] - sel_b)
+
+    # token append into every loop's tail, and the 64-row flush of every loop
+    t = timed(lambda: [qkv.kv_append_tail(ly["c"], 0, n, ly["kn"], ly["vn"], s) for ly in layers])
+    out["kv_append_tail (all loops)"] = row(t, L, append_bytes, "latency")
+    for r in range(w.R):
+        def fl(ly, r=r):
+            f = ly["flush"][r]
+            if f is None:
+                qkv.kv_encode_loop(ly["c"], r + 1, nb, 64, stream=s)
+            else:
+                qkv.kv_encode_loop(ly["c"], r + 1, nb, 64, f[0], f[1], stream=s)
+        t = timed(lambda: [fl(ly) for ly in layers])
+        out[f"kv_encode_loop flush loop {r + 1}"] = row(t, L, flush_loop_bytes[r], "latency")
+
+    # bulk encode of a whole prompt, loop by loop, into a fresh cache
+    K, V, act = synth.gen_layer_torch(w, 4242)
+    c = qcache.LayerCache(w.B, w.H, w.d, w.R, layers[0]["c"].cap, dense=dense)
+    for r in range(w.R):
+        c.act[r, :, :n] = np.asarray(act[r])
+    calls = []
+    for r in range(w.R):
+        if dense[r]:
+            ks, vs = K[r][:, :, :nb].contiguous(), V[r][:, :, :nb].contiguous()
+            calls.append((r, None, None, ks, vs))
+        else:
+            ap, na = c._active_lists(r, 0, nb)
+            ks = torch.zeros((w.B, w.H, nb, w.d), dtype=torch.bfloat16, device="cuda")
+            vs = torch.zeros_like(ks)
+            for b in range(w.B):
+                cnt = int(na[b])
+                rows_ = torch.from_numpy(ap[b, :cnt].astype(np.int64)).cuda()
+                ks[b, :, :cnt] = K[r][b].index_select(1, rows_)
+                vs[b, :, :cnt] = V[r][b].index_select(1, rows_)
+            calls.append((r, torch.from_numpy(ap).cuda(), torch.from_numpy(na).cuda(), ks, vs))
+    del K, V
+    for r, ap, na, ks, vs in calls:
+        t = timed(lambda: qkv.kv_encode_loop(c, r + 1, 0, nb, ap, na, ks, vs, s), reps=3)
+        stored = [nb if dense[r] else int(act[r][b, :nb].sum()) for b in range(w.B)]
+        nbytes = sum(w.H * bm.encode_bytes(st, w.d, r + 1) for st in stored)
+        out[f"kv_encode_loop bulk loop {r + 1} ({nb} positions)"] = row(t, 1, nbytes)
+    del calls, c
+    torch.cuda.empty_cache()
+    for name, v in out.items():
+        print(f"[bench] {name:40s} {v['us']:9.2f} us  {v['bytes'] / 1e6:8.2f} MB  {v['GBps']:8.1f} GB/s",
+              file=sys.stderr, flush=True)
+    return out
 
 
 def read_traffic():

@@ -29,6 +29,13 @@ def dense_loop_bytes(rows_per_plane, tail_rows: int, n: int, d: int) -> int:
     return b
 
 
+def encode_bytes(rows: int, d: int, loop: int) -> int:
+    """Encoding `rows` stored rows of loop `loop` for one (sequence, head): BF16 K and V rows
+    in, the rows' chain through planes 1..loop-1 re-read to form the residual, the new
+    plane rows written."""
+    return rows * d * 2 * 2 + plane_bytes(rows, d) * loop
+
+
 def select_bytes(n: int, k: int) -> int:
     return n * 4 + 4 + k * 8 + 4        # scores + lse in; idx + p_sel + mass out
 

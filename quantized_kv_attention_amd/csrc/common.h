@@ -70,10 +70,25 @@ __device__ __forceinline__ float wave_max(float v) {
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
     return v;
 }
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m, 64));
+    return v;
+}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     return v;
+}
+
+// Eight bf16 values (16 bytes) to floats.
+__device__ __forceinline__ void bf16x8(const uint4 w, float* f) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = bf16_to_f32(ws[e] & 0xFFFFu);
+        f[2 * e + 1] = bf16_to_f32(ws[e] >> 16);
+    }
 }
 
 // Unpacks 32 codes of one lane (16 bytes; channel 2i low nibble, 2i+1 high nibble)

@@ -43,12 +43,6 @@ __device__ __forceinline__ uint64_t lanes_below() {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m, 64));
-    return v;
-}
-
 // Exclusive prefix sum over the workgroup (one barrier); *total = sum over all threads.
 // sh (kSelWaves words) may be reused after the caller's next barrier.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {

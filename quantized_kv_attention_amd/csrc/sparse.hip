@@ -22,15 +22,6 @@ namespace qkv {
 constexpr int kWaveCols = 16;            // selected columns per wave
 constexpr int kChunk = 4 * kWaveCols;    // selected columns per workgroup
 
-__device__ __forceinline__ void bf16x8(const uint4 w, float* f) {
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        f[2 * e] = bf16_to_f32(ws[e] & 0xFFFFu);
-        f[2 * e + 1] = bf16_to_f32(ws[e] >> 16);
-    }
-}
-
 __device__ __forceinline__ void codes8(uint32_t w, float* c) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
