@@ -35,7 +35,7 @@ template <int D>
 __global__ __launch_bounds__(256) void sparse_chunk_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                            float sm, const int32_t* __restrict__ idx,
                                                            const float* __restrict__ p_sel, int k,
-                                                           float* __restrict__ scores, int ld,
+                                                           float* __restrict__ cs,
                                                            float* __restrict__ part) {
     constexpr int LPC = D / 8;             // lanes per column
     constexpr int CPR = 64 / LPC;          // columns per wave round
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void sparse_chunk_kernel(CacheArg ca, int loop
 #pragma unroll
         for (int m = 1; m < LPC; m <<= 1) s += __shfl_xor(s, m, 64);
         if (!valid) s = -__builtin_huge_valf();
-        else if (prt == 0) scores[(size_t)bh * ld + j] = s;
+        else if (prt == 0) cs[(size_t)bh * k + i] = s;  // raw score of entry i; the combine shifts it
         const float nm = fmaxf(mxw, wave_max(s));
         const float scale = (mxw == -__builtin_huge_valf()) ? 0.f : __expf(mxw - nm);
         const float e = valid ? __expf(s - nm) : 0.f;
@@ -189,26 +189,26 @@ constexpr int kSpCombineThreads = 1024;
 template <int D>
 __global__ __launch_bounds__(kSpCombineThreads) void sparse_combine_kernel(
     const float* __restrict__ part, int nchunk, const float* __restrict__ mass, const float* o_prev,
-    const float* __restrict__ lse, const int32_t* __restrict__ idx, int k, float* __restrict__ scores, int ld,
-    uint16_t* __restrict__ o, float* o32) {
+    const float* __restrict__ lse, const int32_t* __restrict__ idx, const float* __restrict__ cs, int k,
+    float* __restrict__ scores, int ld, uint16_t* __restrict__ o, float* o32) {
     const int bh = blockIdx.x, tid = threadIdx.x;
     __shared__ float red[kSpCombineThreads / 64];
     __shared__ float ua[D], wb[D];
     __shared__ float grp[kSpCombineThreads];
     const float* pp = part + (size_t)bh * nchunk * (2 + 2 * D);
-    // the score shift needs each selected column's current score: fetch those first
+    // the selected columns and their raw scores (entry order), read alongside the partials
     constexpr int kPre = 4;
     float* srow = scores + (size_t)bh * ld;
     const int32_t* id = idx + (size_t)bh * k;
+    const float* cr = cs + (size_t)bh * k;
     int jv[kPre];
     float sv[kPre];
 #pragma unroll
     for (int e = 0; e < kPre; ++e) {
         const int i = tid + e * kSpCombineThreads;
         jv[e] = i < k ? id[i] : -1;
+        sv[e] = i < k ? cr[i] : 0.f;
     }
-#pragma unroll
-    for (int e = 0; e < kPre; ++e) sv[e] = (jv[e] >= 0 && jv[e] < ld) ? srow[jv[e]] : 0.f;
     float M;
     const float L = merge_partials<D, kSpCombineThreads, 8>(pp, nchunk, 2 + 2 * D, true, red, ua, wb, grp, &M);
     const float m = mass[bh];
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kSpCombineThreads) void sparse_combine_kernel(
         if (jv[e] >= 0 && jv[e] < ld) srow[jv[e]] = sv[e] + shift;
     for (int i = tid + kPre * kSpCombineThreads; i < k; i += kSpCombineThreads) {
         const int j = id[i];
-        if (j >= 0 && j < ld) srow[j] += shift;
+        if (j >= 0 && j < ld) srow[j] = cr[i] + shift;
     }
 }
 
@@ -236,9 +236,10 @@ __global__ __launch_bounds__(D) void sparse_copy_kernel(const float* o_prev, uin
     if (o) o[(size_t)bh * D + c] = f32_to_bf16_rne(v);
 }
 
+// workspace: chunk partials [B][H][nchunk][2 + 2D], then the raw selected scores [B][H][k]
 size_t sparse_ws_bytes(int B, int H, int D, int k) {
     const int nchunk = (k + kChunk - 1) / kChunk;
-    return (size_t)B * H * nchunk * (2 + 2 * D) * sizeof(float);
+    return (size_t)B * H * nchunk * (2 + 2 * D) * sizeof(float) + (size_t)B * H * k * sizeof(float);
 }
 
 int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, const int32_t* idx,
@@ -253,14 +254,15 @@ int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, float 
         return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
     }
     float* part = static_cast<float*>(ws);
+    float* cs = part + (size_t)ca.B * ca.H * nchunk * (2 + 2 * D);
     dim3 grid(nchunk, ca.H, ca.B);
     if (D == 128) {
-        sparse_chunk_kernel<128><<<grid, 256, 0, st>>>(ca, loop, q, sm, idx, p_sel, k, scores, ld, part);
-        sparse_combine_kernel<128><<<ca.B * ca.H, kSpCombineThreads, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, k, scores, ld,
+        sparse_chunk_kernel<128><<<grid, 256, 0, st>>>(ca, loop, q, sm, idx, p_sel, k, cs, part);
+        sparse_combine_kernel<128><<<ca.B * ca.H, kSpCombineThreads, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k, scores, ld,
                                                                 o, o32);
     } else {
-        sparse_chunk_kernel<64><<<grid, 256, 0, st>>>(ca, loop, q, sm, idx, p_sel, k, scores, ld, part);
-        sparse_combine_kernel<64><<<ca.B * ca.H, kSpCombineThreads, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, k, scores, ld, o,
+        sparse_chunk_kernel<64><<<grid, 256, 0, st>>>(ca, loop, q, sm, idx, p_sel, k, cs, part);
+        sparse_combine_kernel<64><<<ca.B * ca.H, kSpCombineThreads, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k, scores, ld, o,
                                                                o32);
     }
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
