@@ -4,7 +4,10 @@
 One step = one decode step of every rotated layer, run loop-major as a looped model does
 (loop r over all layers before loop r+1): the new token's K/V appended to every loop's
 BF16 tail (plus, once every 64 steps, the 64-row tail flush into every loop's plane),
-dense attention in loops 1-2, top-k selection and the sparse splice in loops 3-4.
+dense attention in loops 1-2, top-k selection and the sparse splice in loops 3-4.  A
+selection reads only the previous loop's scores, which loop-major order has ready for every
+layer before the sparse loop's first layer, so each sparse loop begins with one
+select_columns call over all layers (layers are that call's batch).
 Eight distinct layer caches (about 200 MB each) rotate so that no loop finds its planes
 in the 256 MB last-level cache.  Steps are replayed from two captured HIP graphs (with and
 without the flush); the context stays at n+1 columns.
@@ -42,8 +45,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="the oracle baseline runs decode steps until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--inline-select", action="store_true",
-                    help="run each column selection on the main stream instead of the side stream")
+    ap.add_argument("--select-per-layer", action="store_true",
+                    help="one select_columns call per layer instead of one per sparse loop for all layers")
     ap.add_argument("--kernel-reps", type=int, default=4, help="timed launches per layer of the dominant kernel")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-entry-point measurements")
     ap.add_argument("--profile-dense", action="store_true",
@@ -108,7 +111,6 @@ def main():
         c = qcache.LayerCache(w.B, w.H, w.d, w.R, cap, dense=dense)
         c.prefill(K, V, act)
         del K, V
-        bufs = qcache.DecodeBuffers(c, max_k=k)
         qs = [dev(x) for x in synth.gen_queries(w, 1000 + l)]
         kn, vn = synth.gen_new_token(w, 1000 + l)
         kn = torch.stack([dev(x).view(w.B, w.H, 1, w.d) for x in kn])  # [R, B, H, 1, d]
@@ -122,14 +124,15 @@ def main():
                 ap, na = c._active_lists(r, nb, nb + 64)
                 flush.append((torch.from_numpy(ap).cuda(), torch.from_numpy(na).cuda()))
         c.n_ctx = n_step
-        layers.append(dict(c=c, b=bufs, q=qs, kn=kn, vn=vn, flush=flush, act=act))
+        layers.append(dict(c=c, q=qs, kn=kn, vn=vn, flush=flush, act=act))
         torch.cuda.synchronize()
+    stack = qcache.LayerStack([ly["c"] for ly in layers], max_k=k)
+    for ly, b in zip(layers, stack.layers):
+        ly["b"] = b
     torch.cuda.empty_cache()
     setup_s = time.time() - t_setup
     print(f"[bench] {L} layer caches of {layers[0]['c'].nbytes() / 1e6:.1f} MB ready in {setup_s:.1f}s "
           f"(n={n_step}, k={k})", file=sys.stderr, flush=True)
-
-    side = None if args.inline_select else qcache.SideSelect()
 
     def step(with_flush):
         for ly in layers:
@@ -143,8 +146,11 @@ def main():
                         qkv.kv_encode_loop(c, r + 1, nb, 64, f[0], f[1])
             qkv.kv_append_tail(c, 0, n, ly["kn"], ly["vn"])  # every loop in one launch
         for loop in range(1, w.R + 1):
+            batched = loop > w.n_dense and not args.select_per_layer
+            if batched:
+                stack.select(loop, k)    # loop `loop`'s selections of every layer in one call
             for ly in layers:
-                qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k, side=side)
+                qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k, selected=batched)
 
     def dense2():
         for ly in layers:
@@ -270,7 +276,7 @@ def main():
 
     rows_out = None
     if not args.no_rows:
-        rows_out = measure_rows(w, layers, dense, n, nb, k, loop_bytes, flush_loop_bytes, append_bytes, args)
+        rows_out = measure_rows(w, layers, stack, dense, n, nb, k, loop_bytes, flush_loop_bytes, append_bytes, args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -293,7 +299,8 @@ def main():
                                f"token retention {w.rho}, {int(w.k_frac * 100)}% key columns in loops "
                                f"{w.n_dense + 1}-{w.R}, INT4 g64 + fp32 scale/zero, 64-token BF16 tail",
                    "layers_rotated": L, "k_columns": k, "step": "append + amortised 64-row flush + R-loop attention",
-                   "selection": "inline" if args.inline_select else "side stream, issued after the previous loop",
+                   "selection": ("one call per layer" if args.select_per_layer
+                                 else f"one call per sparse loop for all {L} layers"),
                    "value_is": "microseconds per decode step of one layer"},
         "hbm_GBps_step": round(gbps_step, 1),
         "pct_peak_step": round(100 * gbps_step / HBM_PEAK_GBPS, 2),
@@ -317,7 +324,7 @@ def _dense_source_hash():
     return h.hexdigest()[:16]
 
 
-def measure_rows(w, layers, dense, n, nb, k, loop_bytes, flush_loop_bytes, append_bytes, args):
+def measure_rows(w, layers, stack, dense, n, nb, k, loop_bytes, flush_loop_bytes, append_bytes, args):
     """Each entry point of the path timed on its own (events around back-to-back calls over
     the rotated layers), with its algorithmic bytes and the fraction of the HBM peak."""
     import numpy as np
@@ -361,7 +368,11 @@ def measure_rows(w, layers, dense, n, nb, k, loop_bytes, flush_loop_bytes, appen
             sel = lambda ly: qkv.select_columns(ly["b"].scores, ly["b"].lse, n + 1, kR(loop),
                                                 *ly["b"].selection(loop, kR(loop)), None, s)
             t = timed(lambda: [sel(ly) for ly in layers])
-            out[f"select_columns loop {loop}"] = row(t, L, w.B * w.H * bm.select_bytes(n + 1, k), "latency")
+            out[f"select_columns loop {loop} (one call per layer)"] = row(t, L, w.B * w.H * bm.select_bytes(n + 1, k),
+                                                                         "latency")
+            t = timed(lambda: stack.select(loop, k, s))
+            out[f"select_columns loop {loop} ({L} layers per call)"] = row(t, L, w.B * w.H * bm.select_bytes(n + 1, k),
+                                                                          "latency")
             def sp(ly):
                 idx, ps, mass = ly["b"].selection(loop, k)
                 qkv.attn_decode_sparse(ly["c"], loop, ly["q"][loop - 1], 1.0, idx, ps, mass, k,

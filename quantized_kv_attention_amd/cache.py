@@ -164,87 +164,114 @@ class LayerCache:
 
 
 class DecodeBuffers:
-    """Per-layer outputs of a decode step: o / o_f32 per loop, scores, lse, selection, workspace."""
+    """Per-layer outputs of a decode step: o / o_f32 per loop, scores, lse, selection, workspace.
 
-    def __init__(self, cache: LayerCache, max_k: int, device="cuda"):
+    A layer of a LayerStack keeps scores, lse and its selections inside the stack's
+    allocations (its rows of a batch of L*B sequences) and shares the stack's workspace."""
+
+    def __init__(self, cache: LayerCache, max_k: int, device="cuda", stack: "LayerStack | None" = None,
+                 layer: int = 0):
         B, H, d, R = cache.B, cache.H, cache.d, cache.R
         self.o = torch.zeros((R, B, H, d), dtype=torch.bfloat16, device=device)
         self.o_f32 = torch.zeros((R, B, H, d), dtype=torch.float32, device=device)
-        self.scores = torch.zeros((B, H, cache.cap), dtype=torch.float32, device=device)
-        self.lse = torch.zeros((B, H), dtype=torch.float32, device=device)
         self.max_k = max(1, max_k)
-        # one selection per loop: idx/p_sel [R, B*H*k used as B x H x k], mass [R, B, H]
-        self.idx = torch.zeros((R, B * H * self.max_k), dtype=torch.int32, device=device)
-        self.p_sel = torch.zeros((R, B * H * self.max_k), dtype=torch.float32, device=device)
-        self.mass = torch.zeros((R, B, H), dtype=torch.float32, device=device)
         self.B, self.H = B, H
-        nbytes = workspace_bytes(B, H, d, cache.cap, self.max_k)
-        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
-        self.pending = {}   # loop -> (k, event) of a selection issued on a side stream
+        if stack is None:
+            self.scores = torch.zeros((B, H, cache.cap), dtype=torch.float32, device=device)
+            self.lse = torch.zeros((B, H), dtype=torch.float32, device=device)
+            # one selection per loop: idx/p_sel [R, B*H*k used as B x H x k], mass [R, B, H]
+            self.idx = torch.zeros((R, B * H * self.max_k), dtype=torch.int32, device=device)
+            self.p_sel = torch.zeros((R, B * H * self.max_k), dtype=torch.float32, device=device)
+            self.mass = torch.zeros((R, B, H), dtype=torch.float32, device=device)
+            nbytes = workspace_bytes(B, H, d, cache.cap, self.max_k)
+            self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+            self.layer = 0
+        else:
+            self.scores = stack.scores[layer * B:(layer + 1) * B]
+            self.lse = stack.lse[layer * B:(layer + 1) * B]
+            self.idx, self.p_sel, self.mass, self.ws = stack.idx, stack.p_sel, stack.mass, stack.ws
+            self.layer = layer
 
     def selection(self, loop: int, k: int):
         """Views (idx, p_sel, mass) of loop `loop`'s selection of k columns."""
         r = loop - 1
         kk = max(k, 1)
         n = self.B * self.H * kk
-        return (self.idx[r, :n].view(self.B, self.H, kk), self.p_sel[r, :n].view(self.B, self.H, kk),
-                self.mass[r])
+        off = self.layer * n
+        return (self.idx[r, off:off + n].view(self.B, self.H, kk),
+                self.p_sel[r, off:off + n].view(self.B, self.H, kk),
+                self.mass[r, self.layer * self.B:(self.layer + 1) * self.B])
+
+
+class LayerStack:
+    """Decode buffers of L layers of one model, laid out as one batch of L*B sequences.
+
+    A looped model runs loop r through every layer before loop r+1 begins, and the
+    selection of loop r+1 reads only loop r's scores and lse.  So once loop r has passed
+    the last layer, one select_columns call over the stacked scores makes the selections
+    of every layer; select_columns treats the L layers as L*B independent sequences.
+    Layer l's k selected columns of loop r sit at idx[r, l*B*H*k : (l+1)*B*H*k]."""
+
+    def __init__(self, caches: list, max_k: int, device="cuda"):
+        c0 = caches[0]
+        for c in caches:
+            assert (c.B, c.H, c.d, c.R, c.cap) == (c0.B, c0.H, c0.d, c0.R, c0.cap), "layers differ in shape"
+        L, B, H, R = len(caches), c0.B, c0.H, c0.R
+        self.caches, self.L, self.B, self.H = list(caches), L, B, H
+        self.max_k = max(1, max_k)
+        self.scores = torch.zeros((L * B, H, c0.cap), dtype=torch.float32, device=device)
+        self.lse = torch.zeros((L * B, H), dtype=torch.float32, device=device)
+        self.idx = torch.zeros((R, L * B * H * self.max_k), dtype=torch.int32, device=device)
+        self.p_sel = torch.zeros((R, L * B * H * self.max_k), dtype=torch.float32, device=device)
+        self.mass = torch.zeros((R, L * B, H), dtype=torch.float32, device=device)
+        self.ws = torch.zeros(workspace_bytes(B, H, c0.d, c0.cap, self.max_k), dtype=torch.uint8, device=device)
+        self.layers = [DecodeBuffers(c, max_k, device, stack=self, layer=l) for l, c in enumerate(caches)]
+
+    def select(self, loop: int, k: int, stream=None):
+        """Selections of loop `loop` for every layer, in one call."""
+        r = loop - 1
+        kk = max(k, 1)
+        n = self.L * self.B * self.H * kk
+        select_columns(self.scores, self.lse, self.caches[0].n_ctx, k, self.idx[r, :n], self.p_sel[r, :n],
+                       self.mass[r], None, stream)
 
 
 def k_columns(frac: float, n: int) -> int:
     return min(n, int(math.ceil(frac * n)))
 
 
-class SideSelect:
-    """Second stream (default priority) for the column selections of sparse loops.
-
-    Loop r+1's selection reads only loop r's scores and lse, so it can start as soon as
-    loop r of the same layer is done, beside whatever the main stream runs next (in a
-    looped model: loop r of the following layers).  The sparse loop waits for it."""
-
-    def __init__(self):
-        self.stream = torch.cuda.Stream()
-
-    def issue(self, cache, bufs, loop, k, main):
-        ev = torch.cuda.Event()
-        ev.record(main)
-        self.stream.wait_event(ev)
-        idx, ps, mass = bufs.selection(loop, k)
-        select_columns(bufs.scores, bufs.lse, cache.n_ctx, k, idx, ps, mass, None, self.stream)
-        done = torch.cuda.Event()
-        done.record(self.stream)
-        bufs.pending[loop] = (k, done)
-
-
 def decode_loop(cache: LayerCache, bufs: DecodeBuffers, loop: int, q, n_dense: int, k: int, sm: float = 1.0,
-                stream=None, side: SideSelect | None = None):
+                stream=None, selected: bool = False):
     """Attention of loop `loop` (1-based) for query q [B, H, d] bf16.
 
-    With `side`, the selection of the next loop is issued on the side stream as soon as
-    this loop's scores are written, and a sparse loop consumes the selection issued for it."""
+    A sparse loop first selects its k columns from the previous loop's scores, unless
+    `selected` says that the selection is already in place (LayerStack.select)."""
     r = loop - 1
     main = torch.cuda.current_stream() if stream is None else stream
     if loop <= n_dense:
         attn_decode_dense(cache, loop, q, sm, bufs.o[r], bufs.o_f32[r], bufs.scores, bufs.lse, bufs.ws, main)
     else:
-        n = cache.n_ctx
         assert k <= bufs.max_k
         idx, ps, mass = bufs.selection(loop, k)
-        pend = bufs.pending.pop(loop, None)
-        if pend is not None and pend[0] == k:
-            main.wait_event(pend[1])
-        else:
-            if pend is not None:
-                main.wait_event(pend[1])   # a stale selection must finish before it is overwritten
-            select_columns(bufs.scores, bufs.lse, n, k, idx, ps, mass, None, main)
+        if not selected:
+            select_columns(bufs.scores, bufs.lse, cache.n_ctx, k, idx, ps, mass, None, main)
         attn_decode_sparse(cache, loop, q, sm, idx, ps, mass, k, bufs.o_f32[r - 1], bufs.lse, bufs.scores,
                            bufs.o[r], bufs.o_f32[r], bufs.ws, main)
-    if side is not None and n_dense <= loop < cache.R:
-        side.issue(cache, bufs, loop + 1, k, main)
 
 
-def decode_step(cache: LayerCache, bufs: DecodeBuffers, q, n_dense: int, k: int, sm: float = 1.0, stream=None,
-                side: SideSelect | None = None):
+def decode_step(cache: LayerCache, bufs: DecodeBuffers, q, n_dense: int, k: int, sm: float = 1.0, stream=None):
     """All loops of one decode step of one layer; q[r] bf16 [B, H, d]."""
     for loop in range(1, cache.R + 1):
-        decode_loop(cache, bufs, loop, q[loop - 1], n_dense, k, sm, stream, side)
+        decode_loop(cache, bufs, loop, q[loop - 1], n_dense, k, sm, stream)
+
+
+def decode_step_stack(stack: LayerStack, qs, n_dense: int, k: int, sm: float = 1.0, stream=None):
+    """One decode step of every layer of a stack, loop-major (loop r through all layers,
+    then loop r+1); qs[l][r] is layer l's loop-(r+1) query.  Each sparse loop starts with
+    one selection call for all layers."""
+    main = torch.cuda.current_stream() if stream is None else stream
+    for loop in range(1, stack.caches[0].R + 1):
+        if loop > n_dense:
+            stack.select(loop, k, main)
+        for l, (c, b) in enumerate(zip(stack.caches, stack.layers)):
+            decode_loop(c, b, loop, qs[l][loop - 1], n_dense, k, sm, main, selected=True)

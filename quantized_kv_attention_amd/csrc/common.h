@@ -155,6 +155,32 @@ constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kRowRor4 = 0x124;   // row_ror:4
 constexpr int kRowRor8 = 0x128;   // row_ror:8
 
+constexpr int kRowMirror = 0x140;       // row_mirror: lane i of a 16-lane row reads lane 15 - i
+constexpr int kRowHalfMirror = 0x141;   // row_half_mirror: lane i of an 8-lane half row reads lane 7 - i
+
+// sum over aligned groups of N = 8 or 16 lanes, in every lane of the group
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    static_assert(N == 8 || N == 16, "8- or 16-lane groups");
+    v += dpp<kQuadXor1>(v);
+    v += dpp<kQuadXor2>(v);
+    v += dpp<kRowHalfMirror>(v);
+    if (N == 16) v += dpp<kRowMirror>(v);
+    return v;
+}
+// max over the whole wave, result in every lane (every lane must be active)
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmaxf(v, dpp<kQuadXor1>(v));
+    v = fmaxf(v, dpp<kQuadXor2>(v));
+    v = fmaxf(v, dpp<kRowHalfMirror>(v));
+    v = fmaxf(v, dpp<kRowMirror>(v));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // sum over the LPR consecutive lanes of a row group (LPR = 2 or 4)
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {

@@ -119,11 +119,10 @@ __global__ __launch_bounds__(256) void sparse_chunk_kernel(CacheArg ca, int loop
         float s = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) s = fmaf(qv[c], kh[c], s);
-#pragma unroll
-        for (int m = 1; m < LPC; m <<= 1) s += __shfl_xor(s, m, 64);
+        s = lane_group_sum<LPC>(s);
         if (!valid) s = -__builtin_huge_valf();
         else if (prt == 0) cs[(size_t)bh * k + i] = s;  // raw score of entry i; the combine shifts it
-        const float nm = fmaxf(mxw, wave_max(s));
+        const float nm = fmaxf(mxw, wave_max_dpp(s));
         const float scale = (mxw == -__builtin_huge_valf()) ? 0.f : __expf(mxw - nm);
         const float e = valid ? __expf(s - nm) : 0.f;
         lw = lw * scale + ((prt == 0) ? e : 0.f);

@@ -117,3 +117,29 @@ def test_host_buffers_and_descriptor_cpu():
     assert b.ws.numel() >= qkv.workspace_bytes(2, 3, 128, 512, 50)
     a, n = c._active_lists(2, 0, 64)
     assert a.shape == (2, 64) and n.shape == (2,)
+
+
+def test_layer_stack_layout_cpu():
+    # layer l of a stack owns rows l*B..(l+1)*B of the stacked scores / lse / mass and the
+    # l-th run of B*H*k entries of each loop's selection: one select_columns call over the
+    # stack (batch L*B) writes exactly the per-layer views
+    import torch
+    from quantized_kv_attention_amd import cache as qcache
+    cs = [qcache.LayerCache(2, 3, 128, 4, 512, device="cpu") for _ in range(3)]
+    st = qcache.LayerStack(cs, max_k=40, device="cpu")
+    assert st.scores.shape == (6, 3, 512) and st.mass.shape == (4, 6, 3)
+    k = 17
+    for l, b in enumerate(st.layers):
+        assert b.scores.data_ptr() == st.scores[2 * l].data_ptr() and b.scores.shape == (2, 3, 512)
+        assert b.lse.data_ptr() == st.lse[2 * l].data_ptr()
+        idx, ps, m = b.selection(3, k)
+        assert idx.shape == (2, 3, k) and m.shape == (2, 3)
+        assert idx.data_ptr() == st.idx[2, l * 2 * 3 * k:].data_ptr()
+        assert ps.data_ptr() == st.p_sel[2, l * 2 * 3 * k:].data_ptr()
+        assert m.data_ptr() == st.mass[2, 2 * l].data_ptr()
+        assert b.ws.data_ptr() == st.ws.data_ptr()
+    # the stacked selection, viewed as [L*B, H, k], is the layers' selections in order
+    st.idx[2, :6 * 3 * k] = torch.arange(6 * 3 * k, dtype=torch.int32)
+    whole = st.idx[2, :6 * 3 * k].view(6, 3, k)
+    for l, b in enumerate(st.layers):
+        assert torch.equal(b.selection(3, k)[0], whole[2 * l:2 * l + 2])

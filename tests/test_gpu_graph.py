@@ -47,35 +47,52 @@ def test_graph_replays_match_eager():
     say("  graph replays equal eager results")
 
 
-def test_side_stream_selection_matches_inline():
-    """Selections issued on the side stream (eager and inside a graph) give the results of
-    the inline schedule bit for bit."""
+def test_layer_stack_matches_per_layer_steps():
+    """Loop-major steps of a three-layer stack, with one selection call per sparse loop for
+    all layers, equal each layer's own step bit for bit (eager and replayed from a graph)."""
     w = dataclasses.replace(synth.WORKLOADS["ctx4k"], H=3)
-    p = Pair(w, n=2100, extra=8)
-    k = w.k_cols(2100)
-    q = [to_dev_bf16(x) for x in p.queries(5)]
-    qcache.decode_step(p.gpu, p.bufs, q, w.n_dense, k)
+    n = 2100
+    k = w.k_cols(n)
+    cap = 64 * ((n + 8 + 64 + 63) // 64)
+    caches, qs = [], []
+    for l in range(3):
+        K, V, act = synth.gen_layer_torch(w, 7 + l, n=n)
+        c = qcache.LayerCache(w.B, w.H, w.d, w.R, cap, dense=[w.rho[r] >= 1.0 for r in range(w.R)])
+        c.prefill(K, V, act)
+        caches.append(c)
+        qs.append([to_dev_bf16(x) for x in synth.gen_queries(w, 30 + l)])
+    ref = []
+    for c, q in zip(caches, qs):
+        b = qcache.DecodeBuffers(c, max_k=k)
+        qcache.decode_step(c, b, q, w.n_dense, k)
+        torch.cuda.synchronize()
+        sel = [[t.clone() for t in b.selection(loop, k)] for loop in range(w.n_dense + 1, w.R + 1)]
+        ref.append((b.o_f32.clone(), b.scores.clone(), b.lse.clone(), sel))
+    stack = qcache.LayerStack(caches, max_k=k)
+
+    def check(what):
+        for l, b in enumerate(stack.layers):
+            o, sc, lse, sel = ref[l]
+            assert torch.equal(b.o_f32, o), f"{what}: layer {l} outputs"
+            assert torch.equal(b.scores, sc) and torch.equal(b.lse, lse), f"{what}: layer {l} scores"
+            for loop, tr in zip(range(w.n_dense + 1, w.R + 1), sel):
+                for t, u in zip(b.selection(loop, k), tr):
+                    assert torch.equal(t, u), f"{what}: layer {l} loop {loop} selection"
+
+    qcache.decode_step_stack(stack, qs, w.n_dense, k)
     torch.cuda.synchronize()
-    ref_o, ref_idx, ref_s = p.bufs.o_f32.clone(), p.bufs.idx.clone(), p.bufs.scores.clone()
-    side = qcache.SideSelect()
-    p.bufs.o_f32.zero_()
-    p.bufs.idx.zero_()
-    qcache.decode_step(p.gpu, p.bufs, q, w.n_dense, k, side=side)
-    torch.cuda.synchronize()
-    assert torch.equal(p.bufs.o_f32, ref_o) and torch.equal(p.bufs.idx, ref_idx)
-    assert torch.equal(p.bufs.scores, ref_s)
-    assert not p.bufs.pending
+    check("eager")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        qcache.decode_step(p.gpu, p.bufs, q, w.n_dense, k, side=side)
+        qcache.decode_step_stack(stack, qs, w.n_dense, k)
     for rep in range(3):
-        p.bufs.o_f32.zero_()
-        p.bufs.idx.zero_()
+        stack.idx.zero_()
+        for b in stack.layers:
+            b.o_f32.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(p.bufs.o_f32, ref_o), f"replay {rep}"
-        assert torch.equal(p.bufs.idx, ref_idx), f"replay {rep}"
-        qcache.decode_step(p.gpu, p.bufs, q, w.n_dense, k)   # eager work between replays
+        check(f"replay {rep}")
+        qcache.decode_step_stack(stack, qs, w.n_dense, k)   # eager work between replays
         torch.cuda.synchronize()
-    say("  side-stream selections equal the inline schedule")
+    say("  stacked loop-major steps equal per-layer steps")
