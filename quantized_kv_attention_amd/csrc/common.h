@@ -65,20 +65,61 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ---- cross-lane helpers without LDS traffic ----
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;         // row_ror:4
+constexpr int kRowRor8 = 0x128;         // row_ror:8 (lane i of a 16-lane row reads lane i ^ 8)
+constexpr int kRowMirror = 0x140;       // row_mirror: lane i of a 16-lane row reads lane 15 - i
+constexpr int kRowHalfMirror = 0x141;   // row_half_mirror: lane i of an 8-lane half row reads lane 7 - i
+
+// The values of lane l and of lane l ^ 16 (resp. l ^ 32), in some order, from gfx950's
+// v_permlane16_swap / v_permlane32_swap with both operands equal: a VALU exchange across
+// 16-lane rows (resp. wave halves).
+__device__ __forceinline__ float2 pair_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float2 pair_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float v) { const float2 p = pair_xor16(v); return p.x + p.y; }
+__device__ __forceinline__ float add_xor32(float v) { const float2 p = pair_xor32(v); return p.x + p.y; }
+
+// Whole-wave reductions, the result in every lane: DPP within each 16-lane row, then the
+// rows through the lane swaps.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
+    v = fmaxf(v, dpp<kQuadXor1>(v));
+    v = fmaxf(v, dpp<kQuadXor2>(v));
+    v = fmaxf(v, dpp<kRowHalfMirror>(v));
+    v = fmaxf(v, dpp<kRowMirror>(v));
+    float2 p = pair_xor16(v);
+    v = fmaxf(p.x, p.y);
+    p = pair_xor32(v);
+    return fmaxf(p.x, p.y);
 }
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m, 64));
-    return v;
+    v = fminf(v, dpp<kQuadXor1>(v));
+    v = fminf(v, dpp<kQuadXor2>(v));
+    v = fminf(v, dpp<kRowHalfMirror>(v));
+    v = fminf(v, dpp<kRowMirror>(v));
+    float2 p = pair_xor16(v);
+    v = fminf(p.x, p.y);
+    p = pair_xor32(v);
+    return fminf(p.x, p.y);
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+    v += dpp<kQuadXor1>(v);
+    v += dpp<kQuadXor2>(v);
+    v += dpp<kRowHalfMirror>(v);
+    v += dpp<kRowMirror>(v);
+    v = add_xor16(v);
+    return add_xor32(v);
 }
 
 // Eight bf16 values (16 bytes) to floats.
@@ -144,20 +185,6 @@ __device__ __forceinline__ void unpack32_codes(const uint4 w, float* c) {
     }
 }
 
-
-// ---- cross-lane helpers (DPP: no LDS traffic) ----
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
-constexpr int kRowRor4 = 0x124;   // row_ror:4
-constexpr int kRowRor8 = 0x128;   // row_ror:8
-
-constexpr int kRowMirror = 0x140;       // row_mirror: lane i of a 16-lane row reads lane 15 - i
-constexpr int kRowHalfMirror = 0x141;   // row_half_mirror: lane i of an 8-lane half row reads lane 7 - i
-
 // sum over aligned groups of N = 8 or 16 lanes, in every lane of the group
 template <int N>
 __device__ __forceinline__ float lane_group_sum(float v) {
@@ -168,19 +195,6 @@ __device__ __forceinline__ float lane_group_sum(float v) {
     if (N == 16) v += dpp<kRowMirror>(v);
     return v;
 }
-// max over the whole wave, result in every lane (every lane must be active)
-__device__ __forceinline__ float wave_max_dpp(float v) {
-    v = fmaxf(v, dpp<kQuadXor1>(v));
-    v = fmaxf(v, dpp<kQuadXor2>(v));
-    v = fmaxf(v, dpp<kRowHalfMirror>(v));
-    v = fmaxf(v, dpp<kRowMirror>(v));
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
 // sum over the LPR consecutive lanes of a row group (LPR = 2 or 4)
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {

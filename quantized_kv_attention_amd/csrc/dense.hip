@@ -385,8 +385,7 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
             v += dpp<kRowRor4>(v);
             v += dpp<kRowRor8>(v);
         }
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
+        v = add_xor32(add_xor16(v));
         acc[k] = v;
     }
     {
@@ -399,8 +398,7 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
             v += dpp<kRowRor4>(v);
             v += dpp<kRowRor8>(v);
         }
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
+        v = add_xor32(add_xor16(v));
         vb = v;
     }
     if (rsub == 0) {

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void sparse_chunk_kernel(CacheArg ca, int loop
         s = lane_group_sum<LPC>(s);
         if (!valid) s = -__builtin_huge_valf();
         else if (prt == 0) cs[(size_t)bh * k + i] = s;  // raw score of entry i; the combine shifts it
-        const float nm = fmaxf(mxw, wave_max_dpp(s));
+        const float nm = fmaxf(mxw, wave_max(s));
         const float scale = (mxw == -__builtin_huge_valf()) ? 0.f : __expf(mxw - nm);
         const float e = valid ? __expf(s - nm) : 0.f;
         lw = lw * scale + ((prt == 0) ? e : 0.f);
@@ -136,12 +136,13 @@ __global__ __launch_bounds__(256) void sparse_chunk_kernel(CacheArg ca, int loop
 
     // wave totals: sum the columns of the wave (lanes with the same channels)
 #pragma unroll
-    for (int m = LPC; m < 64; m <<= 1) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            U[c] += __shfl_xor(U[c], m, 64);
-            W[c] += __shfl_xor(W[c], m, 64);
+    for (int c = 0; c < 8; ++c) {
+        if (LPC == 8) {   // the two column groups of a 16-lane row
+            U[c] += dpp<kRowRor8>(U[c]);
+            W[c] += dpp<kRowRor8>(W[c]);
         }
+        U[c] = add_xor32(add_xor16(U[c]));
+        W[c] = add_xor32(add_xor16(W[c]));
     }
     lw = wave_sum(lw);
     __shared__ float wU[4][D], wW[4][D], wm[4], wl[4];
