@@ -9,18 +9,22 @@
 //
 // Gather layout: a column is handled by d/8 lanes of 8 channels each, so one column's
 // codes (d/2 bytes), key scales and zeros (4d bytes each) are read with coalesced loads.
-// Each wave takes 16 selected columns (a few columns per round), dequantises each
-// column's key/value chain exactly in registers (base plus the residual planes that
+// Each wave takes three rounds of 64/(d/8) columns (12 columns at d = 128), dequantises
+// each column's key/value chain exactly in registers (base plus the residual planes that
 // store it) and keeps an online softmax; the 4 waves of a workgroup merge into one
-// partial (max, sum, U = sum e_j vhat^(r)_j, W = sum p_j vhat^(r-1)_j) per 64 columns.
+// partial (max, sum, U = sum e_j vhat^(r)_j, W = sum p_j vhat^(r-1)_j) per chunk.  Three
+// rounds per wave keep every wave of a 32K launch resident at once (5 waves per SIMD):
+// the gather is a sequence of dependent loads per round, and fewer rounds per wave with
+// more waves in flight is what shortens it.
 // A second kernel merges the partials of each (sequence, head), writes o and shifts the
 // selected scores.
 #include "launch.h"
 
 namespace qkv {
 
-constexpr int kWaveCols = 16;            // selected columns per wave
-constexpr int kChunk = 4 * kWaveCols;    // selected columns per workgroup
+constexpr int kWaveRounds = 3;                 // column rounds per wave
+// selected columns per workgroup (4 waves): d/8 lanes per column, 64 / (d/8) per round
+constexpr int chunk_cols(int D) { return 4 * kWaveRounds * (64 / (D / 8)); }
 
 __device__ __forceinline__ void codes8(uint32_t w, float* c) {
 #pragma unroll
@@ -39,7 +43,10 @@ __global__ __launch_bounds__(256) void sparse_chunk_kernel(CacheArg ca, int loop
                                                            float* __restrict__ part) {
     constexpr int LPC = D / 8;             // lanes per column
     constexpr int CPR = 64 / LPC;          // columns per wave round
-    constexpr int ROUNDS = kWaveCols / CPR;
+    constexpr int ROUNDS = kWaveRounds;
+    constexpr int kWaveCols = ROUNDS * CPR;
+    constexpr int kChunk = chunk_cols(D);
+    static_assert(kChunk == 4 * kWaveCols, "four waves per chunk");
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cid = lane / LPC, prt = lane % LPC;
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(kSpCombineThreads) void sparse_combine_kernel(
         sv[e] = i < k ? cr[i] : 0.f;
     }
     float M;
-    const float L = merge_partials<D, kSpCombineThreads, 8>(pp, nchunk, 2 + 2 * D, true, red, ua, wb, grp, &M);
+    const float L = merge_partials<D, kSpCombineThreads, 12>(pp, nchunk, 2 + 2 * D, true, red, ua, wb, grp, &M);
     const float m = mass[bh];
     if (tid < D) {
         const float oc = o_prev[(size_t)bh * D + tid] + m * (ua[tid] / L) - wb[tid];
@@ -238,14 +245,14 @@ __global__ __launch_bounds__(D) void sparse_copy_kernel(const float* o_prev, uin
 
 // workspace: chunk partials [B][H][nchunk][2 + 2D], then the raw selected scores [B][H][k]
 size_t sparse_ws_bytes(int B, int H, int D, int k) {
-    const int nchunk = (k + kChunk - 1) / kChunk;
+    const int nchunk = (k + chunk_cols(D) - 1) / chunk_cols(D);
     return (size_t)B * H * nchunk * (2 + 2 * D) * sizeof(float) + (size_t)B * H * k * sizeof(float);
 }
 
 int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, const int32_t* idx,
                   const float* p_sel, const float* mass, int k, const float* o_prev, const float* lse,
                   float* scores, int ld, uint16_t* o, float* o32, void* ws, hipStream_t st) {
-    const int nchunk = (k + kChunk - 1) / kChunk;
+    const int nchunk = (k + chunk_cols(D) - 1) / chunk_cols(D);
     if (nchunk == 0) {
         if (D == 128)
             sparse_copy_kernel<128><<<ca.B * ca.H, 128, 0, st>>>(o_prev, o, o32);
