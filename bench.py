@@ -2,9 +2,10 @@
 """Decode-attention bench: quantized cross-loop KV cache, 32K context, 4 loops, one MI355X.
 
 One step = one decode step of every rotated layer, run loop-major as a looped model does
-(loop r over all layers before loop r+1): the new token's K/V appended to every loop's
-BF16 tail (plus, once every 64 steps, the 64-row tail flush into every loop's plane),
-dense attention in loops 1-2, top-k selection and the sparse splice in loops 3-4.  A
+(loop r over all layers before loop r+1): dense attention in loops 1-2, top-k selection
+and the sparse splice in loops 3-4, each loop's call storing the new token's K/V row of
+that loop in its BF16 tail (plus, once every 64 steps, the 64-row tail flush into every
+loop's plane).  A
 selection reads only the previous loop's scores, which loop-major order has ready for every
 layer before the sparse loop's first layer, so each sparse loop begins with one
 select_columns call over all layers (layers are that call's batch).
@@ -144,13 +145,14 @@ def main():
                         qkv.kv_encode_loop(c, r + 1, nb, 64)
                     else:
                         qkv.kv_encode_loop(c, r + 1, nb, 64, f[0], f[1])
-            qkv.kv_append_tail(c, 0, n, ly["kn"], ly["vn"])  # every loop in one launch
         for loop in range(1, w.R + 1):
             batched = loop > w.n_dense and not args.select_per_layer
             if batched:
                 stack.select(loop, k)    # loop `loop`'s selections of every layer in one call
             for ly in layers:
-                qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k, selected=batched)
+                # the call stores this loop's row of the new token (position n) in the tail
+                qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k, selected=batched,
+                                   k_new=ly["kn"][loop - 1], v_new=ly["vn"][loop - 1])
 
     def dense2():
         for ly in layers:
@@ -301,7 +303,7 @@ def main():
         "config": {"workload": f"{args.workload}: batch {B}, {H} heads x {d}, context {n_step}, {w.R} loops, "
                                f"token retention {w.rho}, {int(w.k_frac * 100)}% key columns in loops "
                                f"{w.n_dense + 1}-{w.R}, INT4 g64 + fp32 scale/zero, 64-token BF16 tail",
-                   "layers_rotated": L, "k_columns": k, "step": "append + amortised 64-row flush + R-loop attention",
+                   "layers_rotated": L, "k_columns": k, "step": "R-loop attention, each loop's call storing the new token's tail row, + amortised 64-row flush",
                    "selection": ("one call per layer" if args.select_per_layer
                                  else f"one call per sparse loop for all {L} layers"),
                    "value_is": "microseconds per decode step of one layer"},

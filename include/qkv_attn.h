@@ -152,13 +152,18 @@ int kv_append_tail(const qkv_cache* cache, int loop, int pos0, int n_rows,
  *   Keys/values of column j are the loop's reconstruction: base plus every residual
  *   plane p <= loop in which j is stored (BF16 tail values for tail columns).
  *   q        device bf16 [batch][heads][head_dim]; sm_scale multiplies the logits.
+ *   k_new, v_new  both NULL, or device bf16 [batch][heads][head_dim]: this loop's key and
+ *            value of the newest position n_ctx - 1 (already counted in n_ctx).  The call
+ *            stores them in the loop's BF16 tail, as kv_append_tail(cache, loop, n_ctx - 1,
+ *            1, k_new, v_new) would, and attends over them in the same launch
+ *            [PyPI Configuration: 64-token BF16 residual tail].
  *   o        device bf16 [batch][heads][head_dim] (may be NULL); o_f32 device fp32 same shape.
  *   scores   device fp32 [batch][heads][ld_scores]: raw logits s_j, j < n_ctx.
  *   lse      device fp32 [batch][heads]: log sum_j exp(s_j).
  */
-int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, float sm_scale,
-                      uint16_t* o, float* o_f32, float* scores, int ld_scores, float* lse,
-                      void* ws, size_t ws_bytes, void* stream);
+int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,
+                      const uint16_t* v_new, float sm_scale, uint16_t* o, float* o_f32, float* scores,
+                      int ld_scores, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * select_columns - top-k columns of each (sequence, head) under the distribution
@@ -185,8 +190,12 @@ int select_columns(const float* scores, int ld_scores, const float* lse, int bat
  *   0 <= k <= n_ctx (k == 0: o = o_prev).
  *   o_prev   device fp32 [batch][heads][head_dim]: previous loop's output (full precision).
  *   lse      device fp32 [batch][heads]: the lse the selection used.
+ *   k_new, v_new  as for attn_decode_dense: loop `loop`'s row of the newest position,
+ *            stored in the loop's tail and used for that column if it is selected (its
+ *            loop-(loop-1) value is read from that loop's tail, written by its own call).
  */
-int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, float sm_scale,
+int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,
+                       const uint16_t* v_new, float sm_scale,
                        const int32_t* idx, const float* p_sel, const float* mass, int k,
                        const float* o_prev, const float* lse, float* scores, int ld_scores,
                        uint16_t* o, float* o_f32, void* ws, size_t ws_bytes, void* stream);

@@ -66,11 +66,11 @@ def lib():
     L.kv_encode_loop.restype = i32
     L.kv_append_tail.argtypes = [cp, i32, i32, i32, vp, vp, vp]
     L.kv_append_tail.restype = i32
-    L.attn_decode_dense.argtypes = [cp, i32, vp, f32, vp, vp, vp, i32, vp, vp, sz, vp]
+    L.attn_decode_dense.argtypes = [cp, i32, vp, vp, vp, f32, vp, vp, vp, i32, vp, vp, sz, vp]
     L.attn_decode_dense.restype = i32
     L.select_columns.argtypes = [vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.select_columns.restype = i32
-    L.attn_decode_sparse.argtypes = [cp, i32, vp, f32, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    L.attn_decode_sparse.argtypes = [cp, i32, vp, vp, vp, f32, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     L.attn_decode_sparse.restype = i32
     _lib = L
     return L
@@ -129,8 +129,11 @@ def kv_append_tail(cache, loop, pos0, k, v, stream=None):
     _check("kv_append_tail", st)
 
 
-def attn_decode_dense(cache, loop, q, sm_scale, o, o_f32, scores, lse, ws, stream=None):
-    st = lib().attn_decode_dense(ctypes.byref(cache.desc), loop, _ptr(q), float(sm_scale), _ptr(o), _ptr(o_f32),
+def attn_decode_dense(cache, loop, q, sm_scale, o, o_f32, scores, lse, ws, stream=None, k_new=None, v_new=None):
+    """k_new / v_new: this loop's row of the newest position n_ctx - 1 ([B, H, d] bf16), stored
+    in the loop's tail by the same call; None when the tail already holds it."""
+    st = lib().attn_decode_dense(ctypes.byref(cache.desc), loop, _ptr(q), _ptr(k_new), _ptr(v_new), float(sm_scale),
+                                 _ptr(o), _ptr(o_f32),
                                  _ptr(scores), scores.shape[-1], _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream))
     _check("attn_decode_dense", st)
@@ -145,9 +148,11 @@ def select_columns(scores, lse, n, k, idx, p_sel, mass, ws=None, stream=None):
 
 
 def attn_decode_sparse(cache, loop, q, sm_scale, idx, p_sel, mass, k, o_prev, lse, scores, o, o_f32, ws,
-                       stream=None):
+                       stream=None, k_new=None, v_new=None):
+    """k_new / v_new as for attn_decode_dense."""
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    st = lib().attn_decode_sparse(ctypes.byref(cache.desc), loop, _ptr(q), float(sm_scale), _ptr(idx), _ptr(p_sel),
+    st = lib().attn_decode_sparse(ctypes.byref(cache.desc), loop, _ptr(q), _ptr(k_new), _ptr(v_new), float(sm_scale),
+                                  _ptr(idx), _ptr(p_sel),
                                   _ptr(mass), k, _ptr(o_prev), _ptr(lse), _ptr(scores), scores.shape[-1], _ptr(o),
                                   _ptr(o_f32), _ptr(ws), wsb, _stream(stream))
     _check("attn_decode_sparse", st)

@@ -144,6 +144,28 @@ class LayerCache:
         64 positions are first encoded into every loop's plane, loops in order.
         """
         t = self.n_ctx
+        self._flush_before(t, stream)
+        self.act[:, :, t] = True
+        if torch.is_tensor(k_new) and k_new.dim() == 5:
+            kv_append_tail(self, 0, t, k_new, v_new, stream=stream)  # [R, B, H, 1, d], one launch
+        else:
+            ks = torch.stack([x.reshape(self.B, self.H, 1, self.d) for x in k_new])
+            vs = torch.stack([x.reshape(self.B, self.H, 1, self.d) for x in v_new])
+            kv_append_tail(self, 0, t, ks, vs, stream=stream)
+        self.n_ctx = t + 1
+
+    def advance_token(self, stream=None):
+        """Counts the generated token at position n_ctx without writing its rows: each loop's
+        attention call of the step stores its own row (k_new / v_new of decode_loop).
+        Flushes the tail first if it is full, as append_token does."""
+        t = self.n_ctx
+        self._flush_before(t, stream)
+        self.act[:, :, t] = True
+        self.n_ctx = t + 1
+
+    def _flush_before(self, t, stream):
+        """If adding position t moves the body boundary, encodes the tail's 64 oldest
+        positions into every loop's plane, loops in order."""
         nb_old, nb_new = body_len(t), body_len(t + 1)
         if nb_new > nb_old:
             for r in range(self.R):
@@ -153,14 +175,6 @@ class LayerCache:
                     act_pos, n_act = self._active_lists(r, nb_old, nb_old + GROUP)
                     kv_encode_loop(self, r + 1, nb_old, GROUP, torch.from_numpy(act_pos).to(self.device),
                                    torch.from_numpy(n_act).to(self.device), stream=stream)
-        self.act[:, :, t] = True
-        if torch.is_tensor(k_new) and k_new.dim() == 5:
-            kv_append_tail(self, 0, t, k_new, v_new, stream=stream)  # [R, B, H, 1, d], one launch
-        else:
-            ks = torch.stack([x.reshape(self.B, self.H, 1, self.d) for x in k_new])
-            vs = torch.stack([x.reshape(self.B, self.H, 1, self.d) for x in v_new])
-            kv_append_tail(self, 0, t, ks, vs, stream=stream)
-        self.n_ctx = t + 1
 
 
 class DecodeBuffers:
@@ -241,37 +255,47 @@ def k_columns(frac: float, n: int) -> int:
 
 
 def decode_loop(cache: LayerCache, bufs: DecodeBuffers, loop: int, q, n_dense: int, k: int, sm: float = 1.0,
-                stream=None, selected: bool = False):
+                stream=None, selected: bool = False, k_new=None, v_new=None):
     """Attention of loop `loop` (1-based) for query q [B, H, d] bf16.
 
     A sparse loop first selects its k columns from the previous loop's scores, unless
-    `selected` says that the selection is already in place (LayerStack.select)."""
+    `selected` says that the selection is already in place (LayerStack.select).
+    k_new / v_new ([B, H, d] bf16): this loop's row of the newest position, stored in the
+    loop's tail by the attention call itself (after LayerCache.advance_token)."""
     r = loop - 1
     main = torch.cuda.current_stream() if stream is None else stream
     if loop <= n_dense:
-        attn_decode_dense(cache, loop, q, sm, bufs.o[r], bufs.o_f32[r], bufs.scores, bufs.lse, bufs.ws, main)
+        attn_decode_dense(cache, loop, q, sm, bufs.o[r], bufs.o_f32[r], bufs.scores, bufs.lse, bufs.ws, main,
+                          k_new=k_new, v_new=v_new)
     else:
         assert k <= bufs.max_k
         idx, ps, mass = bufs.selection(loop, k)
         if not selected:
             select_columns(bufs.scores, bufs.lse, cache.n_ctx, k, idx, ps, mass, None, main)
         attn_decode_sparse(cache, loop, q, sm, idx, ps, mass, k, bufs.o_f32[r - 1], bufs.lse, bufs.scores,
-                           bufs.o[r], bufs.o_f32[r], bufs.ws, main)
+                           bufs.o[r], bufs.o_f32[r], bufs.ws, main, k_new=k_new, v_new=v_new)
 
 
-def decode_step(cache: LayerCache, bufs: DecodeBuffers, q, n_dense: int, k: int, sm: float = 1.0, stream=None):
-    """All loops of one decode step of one layer; q[r] bf16 [B, H, d]."""
+def decode_step(cache: LayerCache, bufs: DecodeBuffers, q, n_dense: int, k: int, sm: float = 1.0, stream=None,
+                k_new=None, v_new=None):
+    """All loops of one decode step of one layer; q[r] bf16 [B, H, d].  With k_new / v_new
+    (per loop, [B, H, d] bf16) each loop's call stores its row of the newest position."""
     for loop in range(1, cache.R + 1):
-        decode_loop(cache, bufs, loop, q[loop - 1], n_dense, k, sm, stream)
+        kn = None if k_new is None else k_new[loop - 1]
+        vn = None if v_new is None else v_new[loop - 1]
+        decode_loop(cache, bufs, loop, q[loop - 1], n_dense, k, sm, stream, k_new=kn, v_new=vn)
 
 
-def decode_step_stack(stack: LayerStack, qs, n_dense: int, k: int, sm: float = 1.0, stream=None):
+def decode_step_stack(stack: LayerStack, qs, n_dense: int, k: int, sm: float = 1.0, stream=None,
+                      k_new=None, v_new=None):
     """One decode step of every layer of a stack, loop-major (loop r through all layers,
     then loop r+1); qs[l][r] is layer l's loop-(r+1) query.  Each sparse loop starts with
-    one selection call for all layers."""
+    one selection call for all layers.  k_new[l][r] / v_new[l][r]: as for decode_step."""
     main = torch.cuda.current_stream() if stream is None else stream
     for loop in range(1, stack.caches[0].R + 1):
         if loop > n_dense:
             stack.select(loop, k, main)
         for l, (c, b) in enumerate(zip(stack.caches, stack.layers)):
-            decode_loop(c, b, loop, qs[l][loop - 1], n_dense, k, sm, main, selected=True)
+            kn = None if k_new is None else k_new[l][loop - 1]
+            vn = None if v_new is None else v_new[l][loop - 1]
+            decode_loop(c, b, loop, qs[l][loop - 1], n_dense, k, sm, main, selected=True, k_new=kn, v_new=vn)

@@ -137,9 +137,9 @@ int kv_append_tail(const qkv_cache* cache, int loop, int pos0, int n_rows, const
                          cache->tail_v[loop - 1], to_stream(stream));
 }
 
-int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, float sm_scale, uint16_t* o,
-                      float* o_f32, float* scores, int ld_scores, float* lse, void* ws, size_t ws_bytes,
-                      void* stream) {
+int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,
+                      const uint16_t* v_new, float sm_scale, uint16_t* o, float* o_f32, float* scores,
+                      int ld_scores, float* lse, void* ws, size_t ws_bytes, void* stream) {
     CacheArg a;
     int st = make_arg(cache, &a);
     if (st) return st;
@@ -147,10 +147,12 @@ int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, float
     if (cache->n_ctx < 1) return QKV_EINVAL;
     if (!q || !o_f32 || !scores || !lse || ld_scores < cache->n_ctx) return QKV_EINVAL;
     if (!aligned16(q) || !aligned16(o_f32) || (o && !aligned16(o))) return QKV_EINVAL;
+    if ((k_new == nullptr) != (v_new == nullptr) || (k_new && (!aligned16(k_new) || !aligned16(v_new))))
+        return QKV_EINVAL;
     const size_t need = dense_ws_bytes(cache->batch, cache->heads, cache->head_dim, a.n_body);
     if (!ws || ws_bytes < need) return QKV_EWORKSPACE;
-    return launch_dense(a, cache->head_dim, loop, q, sm_scale, o, o_f32, scores, ld_scores, lse, ws,
-                        to_stream(stream));
+    return launch_dense(a, cache->head_dim, loop, q, NewRow{k_new, v_new}, sm_scale, o, o_f32, scores, ld_scores,
+                        lse, ws, to_stream(stream));
 }
 
 int select_columns(const float* scores, int ld_scores, const float* lse, int batch, int heads, int n, int k,
@@ -162,7 +164,8 @@ int select_columns(const float* scores, int ld_scores, const float* lse, int bat
     return launch_select(scores, ld_scores, lse, batch, heads, n, k, idx, p_sel, mass, ws, to_stream(stream));
 }
 
-int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, float sm_scale, const int32_t* idx,
+int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,
+                       const uint16_t* v_new, float sm_scale, const int32_t* idx,
                        const float* p_sel, const float* mass, int k, const float* o_prev, const float* lse,
                        float* scores, int ld_scores, uint16_t* o, float* o_f32, void* ws, size_t ws_bytes,
                        void* stream) {
@@ -174,10 +177,12 @@ int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, floa
     if (!q || !o_prev || !lse || !scores || !o_f32 || ld_scores < cache->n_ctx) return QKV_EINVAL;
     if (k > 0 && (!idx || !p_sel || !mass)) return QKV_EINVAL;
     if (!aligned16(q) || (o && !aligned16(o))) return QKV_EINVAL;
+    if ((k_new == nullptr) != (v_new == nullptr) || (k_new && (!aligned16(k_new) || !aligned16(v_new))))
+        return QKV_EINVAL;
     const size_t need = sparse_ws_bytes(cache->batch, cache->heads, cache->head_dim, k);
     if (k > 0 && (!ws || ws_bytes < need)) return QKV_EWORKSPACE;
-    return launch_sparse(a, cache->head_dim, loop, q, sm_scale, idx, p_sel, mass, k, o_prev, lse, scores, ld_scores,
-                         o, o_f32, ws, to_stream(stream));
+    return launch_sparse(a, cache->head_dim, loop, q, NewRow{k_new, v_new}, sm_scale, idx, p_sel, mass, k, o_prev,
+                         lse, scores, ld_scores, o, o_f32, ws, to_stream(stream));
 }
 
 }  // extern "C"

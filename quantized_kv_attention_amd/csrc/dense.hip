@@ -100,7 +100,7 @@ __device__ __forceinline__ void vpass_block(const uint8_t* bp, int prt, int rsub
 // by one.
 template <int D, int NPRE>
 __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
-                                                          float sm, float* __restrict__ scores, int ld,
+                                                          NewRow nr, float sm, float* __restrict__ scores, int ld,
                                                           float* __restrict__ part, int nsplit, int spb) {
     constexpr int LPR = Block<D>::kLpr, RPI = Block<D>::kRpi, NLD = 64 / RPI;
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -124,6 +124,15 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
     const int j0 = blk0 * 64, L = nb * 64;
     const bool has_tail = (s == nsplit - 1);
     const int T = has_tail ? ca.n_ctx - ca.n_body : 0;  // tail rows land in logit[L + i]
+    // The newest position's row (if given) goes into the tail ring first; this workgroup
+    // reads the tail only after several barriers, and no other workgroup reads it.
+    if (has_tail && nr.k) {
+        const size_t dst = ((size_t)(b * ca.H + h) * kTail + (ca.n_ctx - 1) % kTail) * D;
+        for (int c = threadIdx.x; c < D; c += 256) {
+            const_cast<uint16_t*>(ca.tail_k[loop - 1])[dst + c] = nr.k[(size_t)(b * ca.H + h) * D + c];
+            const_cast<uint16_t*>(ca.tail_v[loop - 1])[dst + c] = nr.v[(size_t)(b * ca.H + h) * D + c];
+        }
+    }
     const int nstart = ca.cap_ctx / 64 + 1;
     const int blkA = blk0 + wave;                         // this wave's first block
     // Prefetches are unconditional (a branch around them makes the compiler wait for them at
@@ -466,25 +475,25 @@ size_t dense_ws_bytes(int B, int H, int D, int n_body) {
 }
 
 template <int D>
-static void launch_dense_d(const CacheArg& ca, int loop, const uint16_t* q, float sm, uint16_t* o, float* o32,
+static void launch_dense_d(const CacheArg& ca, int loop, const uint16_t* q, NewRow nr, float sm, uint16_t* o, float* o32,
                            float* scores, int ld, float* lse, float* part, hipStream_t st) {
     const DensePlan pl = dense_plan(ca.B, ca.H, ca.n_body);
     dim3 grid(pl.nsplit, ca.H, ca.B);
     // plane 1 (the base) is always dense; plane 2 joins it when it is dense too
     if (loop >= 2 && ca.p[1].dense)
-        dense_split_kernel<D, 2><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
+        dense_split_kernel<D, 2><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit, pl.spb);
     else
-        dense_split_kernel<D, 1><<<grid, 256, 0, st>>>(ca, loop, q, sm, scores, ld, part, pl.nsplit, pl.spb);
+        dense_split_kernel<D, 1><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit, pl.spb);
     dense_combine_kernel<D><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit, o, o32, lse);
 }
 
-int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, uint16_t* o, float* o32,
+int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, uint16_t* o, float* o32,
                  float* scores, int ld, float* lse, void* ws, hipStream_t st) {
     float* part = static_cast<float*>(ws);
     if (D == 128)
-        launch_dense_d<128>(ca, loop, q, sm, o, o32, scores, ld, lse, part, st);
+        launch_dense_d<128>(ca, loop, q, nr, sm, o, o32, scores, ld, lse, part, st);
     else
-        launch_dense_d<64>(ca, loop, q, sm, o, o32, scores, ld, lse, part, st);
+        launch_dense_d<64>(ca, loop, q, nr, sm, o, o32, scores, ld, lse, part, st);
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
 }
 

@@ -13,6 +13,12 @@ int launch_append(int B, int H, int D, int pos0, int n_rows, const uint16_t* k, 
 int launch_append_all(const CacheArg& ca, int D, int pos0, int n_rows, const uint16_t* k, const uint16_t* v,
                       hipStream_t st);
 
+// The newest position's row of one loop (bf16 [B][H][D] each), or both NULL.
+struct NewRow {
+    const uint16_t* k;
+    const uint16_t* v;
+};
+
 // split-KV plan of the dense reader: blocks per split and number of body splits
 struct DensePlan {
     int spb;
@@ -20,7 +26,7 @@ struct DensePlan {
 };
 DensePlan dense_plan(int B, int H, int n_body);
 size_t dense_ws_bytes(int B, int H, int D, int n_body);
-int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, uint16_t* o, float* o32,
+int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, uint16_t* o, float* o32,
                  float* scores, int ld, float* lse, void* ws, hipStream_t st);
 
 size_t select_ws_bytes(int B, int H, int n);
@@ -28,7 +34,7 @@ int launch_select(const float* scores, int ld, const float* lse, int B, int H, i
                   float* p_sel, float* mass, void* ws, hipStream_t st);
 
 size_t sparse_ws_bytes(int B, int H, int D, int k);
-int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, const int32_t* idx,
+int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, const int32_t* idx,
                   const float* p_sel, const float* mass, int k, const float* o_prev, const float* lse,
                   float* scores, int ld, uint16_t* o, float* o32, void* ws, hipStream_t st);
 

@@ -35,9 +35,21 @@ __device__ __forceinline__ void codes8(uint32_t w, float* c) {
     }
 }
 
+// Stores the newest position's row (nr, [B*H][D]) of (sequence, head) bh in tail ring slot
+// `slot` of tk / tv ([B*H][kTail][D]).
+template <int D>
+__device__ __forceinline__ void store_new_row(NewRow nr, uint16_t* tk, uint16_t* tv, int bh, int slot) {
+    if (!nr.k) return;
+    const size_t dst = ((size_t)bh * kTail + slot) * D;
+    for (int c = threadIdx.x; c < D; c += blockDim.x) {
+        tk[dst + c] = nr.k[(size_t)bh * D + c];
+        tv[dst + c] = nr.v[(size_t)bh * D + c];
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void sparse_chunk_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
-                                                           float sm, const int32_t* __restrict__ idx,
+                                                           NewRow nr, float sm, const int32_t* __restrict__ idx,
                                                            const float* __restrict__ p_sel, int k,
                                                            float* __restrict__ cs,
                                                            float* __restrict__ part) {
@@ -49,6 +61,14 @@ __global__ __launch_bounds__(256) void sparse_chunk_kernel(CacheArg ca, int loop
     static_assert(kChunk == 4 * kWaveCols, "four waves per chunk");
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The newest position is the largest column, so when it is selected it is the last entry
+    // of the last chunk: that workgroup stores the position's row (if given) in the tail ring
+    // before any of its waves reads the tail, and no other workgroup reads that slot.
+    if (nr.k && chunk == (int)gridDim.x - 1) {
+        store_new_row<D>(nr, const_cast<uint16_t*>(ca.tail_k[loop - 1]), const_cast<uint16_t*>(ca.tail_v[loop - 1]),
+                         b * ca.H + h, (ca.n_ctx - 1) % kTail);
+        __syncthreads();
+    }
     const int cid = lane / LPC, prt = lane % LPC;
     const int bh = b * ca.H + h;
     const int cap = ca.cap_ctx;
@@ -236,8 +256,10 @@ __global__ __launch_bounds__(kSpCombineThreads) void sparse_combine_kernel(
 
 // k == 0: the output is the previous loop's output
 template <int D>
-__global__ __launch_bounds__(D) void sparse_copy_kernel(const float* o_prev, uint16_t* __restrict__ o, float* o32) {
+__global__ __launch_bounds__(D) void sparse_copy_kernel(const float* o_prev, uint16_t* __restrict__ o, float* o32,
+                                                        NewRow nr, uint16_t* tk, uint16_t* tv, int slot) {
     const int bh = blockIdx.x, c = threadIdx.x;
+    store_new_row<D>(nr, tk, tv, bh, slot);
     const float v = o_prev[(size_t)bh * D + c];
     o32[(size_t)bh * D + c] = v;
     if (o) o[(size_t)bh * D + c] = f32_to_bf16_rne(v);
@@ -249,28 +271,31 @@ size_t sparse_ws_bytes(int B, int H, int D, int k) {
     return (size_t)B * H * nchunk * (2 + 2 * D) * sizeof(float) + (size_t)B * H * k * sizeof(float);
 }
 
-int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, float sm, const int32_t* idx,
+int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, const int32_t* idx,
                   const float* p_sel, const float* mass, int k, const float* o_prev, const float* lse,
                   float* scores, int ld, uint16_t* o, float* o32, void* ws, hipStream_t st) {
     const int nchunk = (k + chunk_cols(D) - 1) / chunk_cols(D);
+    uint16_t* tk = const_cast<uint16_t*>(ca.tail_k[loop - 1]);
+    uint16_t* tv = const_cast<uint16_t*>(ca.tail_v[loop - 1]);
+    const int slot = (ca.n_ctx - 1) % kTail;
     if (nchunk == 0) {
         if (D == 128)
-            sparse_copy_kernel<128><<<ca.B * ca.H, 128, 0, st>>>(o_prev, o, o32);
+            sparse_copy_kernel<128><<<ca.B * ca.H, 128, 0, st>>>(o_prev, o, o32, nr, tk, tv, slot);
         else
-            sparse_copy_kernel<64><<<ca.B * ca.H, 64, 0, st>>>(o_prev, o, o32);
+            sparse_copy_kernel<64><<<ca.B * ca.H, 64, 0, st>>>(o_prev, o, o32, nr, tk, tv, slot);
         return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
     }
     float* part = static_cast<float*>(ws);
     float* cs = part + (size_t)ca.B * ca.H * nchunk * (2 + 2 * D);
     dim3 grid(nchunk, ca.H, ca.B);
     if (D == 128) {
-        sparse_chunk_kernel<128><<<grid, 256, 0, st>>>(ca, loop, q, sm, idx, p_sel, k, cs, part);
-        sparse_combine_kernel<128><<<ca.B * ca.H, kSpCombineThreads, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k, scores, ld,
-                                                                o, o32);
+        sparse_chunk_kernel<128><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
+        sparse_combine_kernel<128><<<ca.B * ca.H, kSpCombineThreads, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
+                                                                              scores, ld, o, o32);
     } else {
-        sparse_chunk_kernel<64><<<grid, 256, 0, st>>>(ca, loop, q, sm, idx, p_sel, k, cs, part);
-        sparse_combine_kernel<64><<<ca.B * ca.H, kSpCombineThreads, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k, scores, ld, o,
-                                                               o32);
+        sparse_chunk_kernel<64><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
+        sparse_combine_kernel<64><<<ca.B * ca.H, kSpCombineThreads, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
+                                                                             scores, ld, o, o32);
     }
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
 }

@@ -65,7 +65,7 @@ def test_descriptor_validation(mut, expect):
     L = qkv.lib()
     d = _desc(**mut)
     vp = ctypes.c_void_p
-    st = L.attn_decode_dense(ctypes.byref(d), 1, vp(16), 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None)
+    st = L.attn_decode_dense(ctypes.byref(d), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None)
     assert st == expect
 
 
@@ -74,14 +74,18 @@ def test_argument_validation():
     vp = ctypes.c_void_p
     d = _desc()
     # loop out of range, null query, misaligned pointer, short workspace
-    assert L.attn_decode_dense(ctypes.byref(d), 3, vp(16), 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
-    assert L.attn_decode_dense(ctypes.byref(d), 1, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
-    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(18), 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
-    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), 1.0, None, vp(16), vp(16), 100, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
-    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 16, None) == qkv.QKV_EWORKSPACE
+    assert L.attn_decode_dense(ctypes.byref(d), 3, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, None, None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(18), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 100, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 16, None) == qkv.QKV_EWORKSPACE
+    # the newest position's row: both pointers or neither, 16-byte aligned
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), vp(16), None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), vp(16), vp(20), 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_sparse(ctypes.byref(d), 2, vp(16), None, vp(16), 1.0, vp(16), vp(16), vp(16), 4, vp(16), vp(16), vp(16), 256, None, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
     # sparse loop 1 is not allowed; k beyond the context is not allowed
-    assert L.attn_decode_sparse(ctypes.byref(d), 1, vp(16), 1.0, vp(16), vp(16), vp(16), 4, vp(16), vp(16), vp(16), 256, None, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
-    assert L.attn_decode_sparse(ctypes.byref(d), 2, vp(16), 1.0, vp(16), vp(16), vp(16), 300, vp(16), vp(16), vp(16), 256, None, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_sparse(ctypes.byref(d), 1, vp(16), None, None, 1.0, vp(16), vp(16), vp(16), 4, vp(16), vp(16), vp(16), 256, None, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_sparse(ctypes.byref(d), 2, vp(16), None, None, 1.0, vp(16), vp(16), vp(16), 300, vp(16), vp(16), vp(16), 256, None, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
     # encode: unaligned range, dense plane with an active list, beyond capacity, tail rows not in the tail
     assert L.kv_encode_loop(ctypes.byref(d), 1, 32, 64, None, None, 0, vp(16), vp(16), 64, None) == qkv.QKV_EINVAL
     assert L.kv_encode_loop(ctypes.byref(d), 1, 0, 64, vp(16), vp(16), 64, vp(16), vp(16), 64, None) == qkv.QKV_EINVAL
