@@ -24,7 +24,8 @@ namespace qkv {
 
 constexpr int kWaveRounds = 3;                 // column rounds per wave
 // selected columns per workgroup (4 waves): d/8 lanes per column, 64 / (d/8) per round
-constexpr int chunk_cols(int D) { return 4 * kWaveRounds * (64 / (D / 8)); }
+constexpr int kSpWaves = 4;                    // waves per workgroup
+constexpr int chunk_cols(int D) { return kSpWaves * kWaveRounds * (64 / (D / 8)); }
 
 __device__ __forceinline__ void codes8(uint32_t w, float* c) {
 #pragma unroll
@@ -48,7 +49,7 @@ __device__ __forceinline__ void store_new_row(NewRow nr, uint16_t* tk, uint16_t*
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void sparse_chunk_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * kSpWaves) void sparse_chunk_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                            NewRow nr, float sm, const int32_t* __restrict__ idx,
                                                            const float* __restrict__ p_sel, int k,
                                                            float* __restrict__ cs,
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void sparse_chunk_kernel(CacheArg ca, int loop
     constexpr int ROUNDS = kWaveRounds;
     constexpr int kWaveCols = ROUNDS * CPR;
     constexpr int kChunk = chunk_cols(D);
-    static_assert(kChunk == 4 * kWaveCols, "four waves per chunk");
+    static_assert(kChunk == kSpWaves * kWaveCols, "a chunk is the workgroup's columns");
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // The newest position is the largest column, so when it is selected it is the last entry
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(256) void sparse_chunk_kernel(CacheArg ca, int loop
         W[c] = add_xor32(add_xor16(W[c]));
     }
     lw = wave_sum(lw);
-    __shared__ float wU[4][D], wW[4][D], wm[4], wl[4];
+    __shared__ float wU[kSpWaves][D], wW[kSpWaves][D], wm[kSpWaves], wl[kSpWaves];
     if (cid == 0) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -185,24 +186,26 @@ __global__ __launch_bounds__(256) void sparse_chunk_kernel(CacheArg ca, int loop
         wl[wave] = lw;
     }
     __syncthreads();
-    const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+    float M = wm[0];
+#pragma unroll
+    for (int w = 1; w < kSpWaves; ++w) M = fmaxf(M, wm[w]);
     float* out = part + ((size_t)bh * gridDim.x + chunk) * (2 + 2 * D);
-    for (int t = tid; t < 2 * D; t += 256) {
+    for (int t = tid; t < 2 * D; t += 64 * kSpWaves) {
         float a = 0.f;
         if (t < D) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
+            for (int w = 0; w < kSpWaves; ++w)
                 if (wm[w] != -__builtin_huge_valf()) a = fmaf(wU[w][t], __expf(wm[w] - M), a);
         } else {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) a += wW[w][t - D];
+            for (int w = 0; w < kSpWaves; ++w) a += wW[w][t - D];
         }
         out[2 + t] = a;
     }
     if (tid == 0) {
         float L = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
+        for (int w = 0; w < kSpWaves; ++w)
             if (wm[w] != -__builtin_huge_valf()) L = fmaf(wl[w], __expf(wm[w] - M), L);
         out[0] = M;
         out[1] = L;
@@ -289,11 +292,11 @@ int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow
     float* cs = part + (size_t)ca.B * ca.H * nchunk * (2 + 2 * D);
     dim3 grid(nchunk, ca.H, ca.B);
     if (D == 128) {
-        sparse_chunk_kernel<128><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
+        sparse_chunk_kernel<128><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
         sparse_combine_kernel<128><<<ca.B * ca.H, kSpCombineThreads, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
                                                                               scores, ld, o, o32);
     } else {
-        sparse_chunk_kernel<64><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
+        sparse_chunk_kernel<64><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
         sparse_combine_kernel<64><<<ca.B * ca.H, kSpCombineThreads, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
                                                                              scores, ld, o, o32);
     }
