@@ -7,13 +7,13 @@
 // (up to 40 of them) in registers.  A histogram over 2048 equal-width value bins between
 // the smallest and largest score finds the bin holding the k-th column (bins are a monotone
 // function of the score, so every bin above it is taken whole); the few columns of that
-// bin are ranked exactly, which gives the threshold (score, index).  Each thread then holds
-// its selection as a bit mask, and one scan over per-(row, wave) counts places the
-// selected columns in ascending index order.
+// bin are ranked exactly as 64-bit (key, index) words, which gives the threshold (score,
+// index).  A column is then taken iff it is above the threshold in that order; one scan over
+// per-(row, wave) counts places the selected columns in ascending index order.
 //
 // The fast path is kept small (its unrolled loops carry no mode branches).  Everything
-// else (k >= n, equal or non-finite scores, a crowded threshold bin, contexts beyond 40960
-// columns) goes to plain loops over memory: a 3-pass radix threshold on an
+// else (k >= n, equal, infinite or NaN scores, a crowded threshold bin, contexts beyond
+// 40960 columns) goes to plain loops over memory: a 3-pass radix threshold on an
 // order-preserving integer key and a row-by-row compaction.
 #include "launch.h"
 
@@ -30,6 +30,16 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     uint32_t u = __float_as_uint(x);
     if (u == 0x80000000u) u = 0u;  // -0 == +0
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// inverse of order_key (the key of -0 gives +0)
+__device__ __forceinline__ float key_float(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// (key, index) as one word whose unsigned order is the selection order: larger first
+__device__ __forceinline__ uint64_t sort_word(float x, int j) {
+    return ((uint64_t)order_key(x) << 32) | (uint64_t)(~(uint32_t)j);
 }
 
 __device__ __forceinline__ uint32_t value_bin(float x, float lo, float scale) {
@@ -163,8 +173,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
     __shared__ uint32_t scan_sh[kSelWaves];
     __shared__ float fmin_sh[kSelWaves], fmax_sh[kSelWaves];
     __shared__ uint32_t bcast[4];
-    __shared__ uint32_t cand_key[kCandCap];
-    __shared__ int32_t cand_idx[kCandCap];
+    __shared__ uint64_t cand[kCandCap];
+    __shared__ uint64_t thr_sh;
     __shared__ uint32_t row_off[kSelPerThread * kSelWaves];  // [row][wave]: counts, then offsets
     __shared__ int32_t st_idx[kStage];
     __shared__ float st_p[kStage];
@@ -180,21 +190,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
     bool done = false;  // uniform
 
     if (k < n && E <= kSelPerThread) {
-        // ---- fast path: column j = e * 1024 + tid in v[e] ----
+        // ---- fast path: column j = e * 1024 + tid in v[e] (columns past n repeat column n-1,
+        //      which leaves the extremes unchanged; every later use tests j < n) ----
         float v[kSelPerThread];
 #pragma unroll
-        for (int e = 0; e < kSelPerThread; ++e) {
-            const int j = e * kSelThreads + tid;
-            v[e] = (e < E && j < n) ? sc[j] : 0.f;
-        }
+        for (int e = 0; e < kSelPerThread; ++e) v[e] = sc[min(e * kSelThreads + tid, n - 1)];
         for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
+        for (int i = tid; i < kCandCap; i += kSelThreads) cand[i] = 0;  // padding ranks below everything
         float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+        uint64_t nan_lanes = 0;
 #pragma unroll
-        for (int e = 0; e < kSelPerThread; ++e)
-            if (e < E && e * kSelThreads + tid < n) {
-                mn = fminf(mn, v[e]);
-                mx = fmaxf(mx, v[e]);
-            }
+        for (int e = 0; e < kSelPerThread; ++e) {
+            mn = fminf(mn, v[e]);
+            mx = fmaxf(mx, v[e]);
+            nan_lanes |= __ballot(__builtin_isnan(v[e]));
+        }
+        if (nan_lanes) mx = __builtin_huge_valf();  // NaN: the key order of the memory paths decides
         mn = wave_min(mn);
         mx = wave_max(mx);
         if (lane == 0) {
@@ -214,7 +225,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
         if (range > 0.f && __builtin_isfinite(range) && __builtin_isfinite(scale)) {
 #pragma unroll
             for (int e = 0; e < kSelPerThread; ++e)
-                if (e < E && e * kSelThreads + tid < n) atomicAdd(&hist[value_bin(v[e], lo, scale)], 1u);
+                if (e * kSelThreads + tid < n) atomicAdd(&hist[value_bin(v[e], lo, scale)], 1u);
             __syncthreads();
             // bin of the k-th largest, counting from the top bin (thread t: bins 2047-2t, 2046-2t)
             const uint32_t b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
@@ -232,52 +243,44 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
             const uint32_t bstar = bcast[0];
             const uint32_t need_in = (uint32_t)k - bcast[1];  // columns taken inside the threshold bin
             if (hist[bstar] <= (uint32_t)kCandCap) {
+                // the threshold bin's columns as (key, index) sort words
 #pragma unroll
                 for (int e = 0; e < kSelPerThread; ++e) {
                     const int j = e * kSelThreads + tid;
-                    if (e < E && j < n && value_bin(v[e], lo, scale) == bstar) {
+                    if (j < n && value_bin(v[e], lo, scale) == bstar) {
                         const uint32_t slot = atomicAdd(&bcast[2], 1u);
-                        cand_key[slot] = order_key(v[e]);
-                        cand_idx[slot] = j;
+                        cand[slot] = sort_word(v[e], j);
                     }
                 }
                 __syncthreads();
-                // exact rank of each candidate under (key descending, index ascending)
+                // the candidate of rank need_in - 1 (bins are monotone in the score, so every
+                // column of a higher bin precedes it and every column of a lower bin follows)
                 const uint32_t c = bcast[2];
+                const uint32_t cpad = (c + 7u) & ~7u;
                 for (uint32_t t = tid; t < c; t += kSelThreads) {
-                    const uint32_t kt = cand_key[t];
-                    const int32_t it = cand_idx[t];
+                    const uint64_t rt = cand[t];
                     uint32_t rank = 0;
-                    for (uint32_t u = 0; u < c; ++u) {
-                        const uint32_t ku = cand_key[u];
-                        rank += (ku > kt || (ku == kt && cand_idx[u] < it)) ? 1u : 0u;
+                    for (uint32_t u = 0; u < cpad; u += 8) {
+#pragma unroll
+                        for (int w = 0; w < 8; ++w) rank += cand[u + w] > rt ? 1u : 0u;
                     }
-                    if (rank == need_in - 1) {
-                        bcast[0] = kt;
-                        bcast[1] = (uint32_t)it;
-                    }
+                    if (rank == need_in - 1) thr_sh = rt;
                 }
                 __syncthreads();
-                const uint32_t tk = bcast[0];
-                const int32_t ti = (int32_t)bcast[1];
-                // selection mask: bit e <=> column e * 1024 + tid is taken
-                uint64_t fm = 0;
+                const uint64_t thr = thr_sh;
+                const float tx = key_float((uint32_t)(thr >> 32));
+                const int ti = (int)~(uint32_t)thr;
+                // taken <=> score above tx, or equal to it at an index <= ti
+                // per-(row, wave) counts (lane e of cnts: row e), one scan, then each position
+                uint32_t cnts = 0;
 #pragma unroll
                 for (int e = 0; e < kSelPerThread; ++e) {
                     const int j = e * kSelThreads + tid;
-                    if (e < E && j < n) {
-                        const uint32_t bn = value_bin(v[e], lo, scale);
-                        const uint32_t key = order_key(v[e]);
-                        if (bn > bstar || (bn == bstar && (key > tk || (key == tk && j <= ti)))) fm |= 1ull << e;
-                    }
+                    const bool f = (v[e] > tx && j < n) || (v[e] == tx && j <= ti);
+                    const uint32_t cnt = (uint32_t)__popcll(__ballot(f));
+                    cnts = lane == e ? cnt : cnts;
                 }
-                // per-(row, wave) counts, one scan over them, then every column's position
-#pragma unroll
-                for (int e = 0; e < kSelPerThread; ++e)
-                    if (e < E) {
-                        const uint64_t bal = __ballot((fm >> e) & 1ull);
-                        if (lane == 0) row_off[e * kSelWaves + wave] = (uint32_t)__popcll(bal);
-                    }
+                if (lane < E) row_off[lane * kSelWaves + wave] = cnts;
                 __syncthreads();
                 const int nrw = E * kSelWaves;
                 uint32_t tot2;
@@ -286,26 +289,29 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
                 __syncthreads();  // every count has been read
                 if (tid < nrw) row_off[tid] = ex;
                 __syncthreads();
+                const uint32_t offs = lane < E ? row_off[lane * kSelWaves + wave] : 0u;
                 const bool stage = k <= kStage;
-                const uint64_t below = lanes_below();
 #pragma unroll
-                for (int e = 0; e < kSelPerThread; ++e)
-                    if (e < E) {
-                        const bool f = (fm >> e) & 1ull;
-                        const uint64_t bal = __ballot(f);
-                        if (f) {
-                            const uint32_t pos = row_off[e * kSelWaves + wave] + (uint32_t)__popcll(bal & below);
-                            const float p = __expf(v[e] - l);
-                            psum += p;
-                            if (stage) {
-                                st_idx[pos] = e * kSelThreads + tid;
-                                st_p[pos] = p;
-                            } else {
-                                id[pos] = e * kSelThreads + tid;
-                                ps[pos] = p;
-                            }
+                for (int e = 0; e < kSelPerThread; ++e) {
+                    const int j = e * kSelThreads + tid;
+                    const bool f = (v[e] > tx && j < n) || (v[e] == tx && j <= ti);
+                    const uint64_t bal = __ballot(f);
+                    const uint32_t base = __builtin_amdgcn_readlane(offs, e);
+                    if (f) {
+                        const uint32_t pos =
+                            base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                        const float p = __expf(v[e] - l);
+                        psum += p;
+                        if (stage) {
+                            st_idx[pos] = j;
+                            st_p[pos] = p;
+                        } else {
+                            id[pos] = j;
+                            ps[pos] = p;
                         }
                     }
+                }
                 if (stage) {
                     __syncthreads();
                     for (int i = tid; i < k; i += kSelThreads) {

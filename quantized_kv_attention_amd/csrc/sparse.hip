@@ -239,15 +239,17 @@ __global__ __launch_bounds__(kSpCombineThreads) void sparse_combine_kernel(
         jv[e] = i < k ? id[i] : -1;
         sv[e] = i < k ? cr[i] : 0.f;
     }
+    // loads that do not depend on the merge go out with it
+    const float m = mass[bh], lse_prev = lse[bh];
+    const float op = tid < D ? o_prev[(size_t)bh * D + tid] : 0.f;
     float M;
     const float L = merge_partials<D, kSpCombineThreads, 12>(pp, nchunk, 2 + 2 * D, true, red, ua, wb, grp, &M);
-    const float m = mass[bh];
     if (tid < D) {
-        const float oc = o_prev[(size_t)bh * D + tid] + m * (ua[tid] / L) - wb[tid];
+        const float oc = op + m * (ua[tid] / L) - wb[tid];
         o32[(size_t)bh * D + tid] = oc;
         if (o) o[(size_t)bh * D + tid] = f32_to_bf16_rne(oc);
     }
-    const float shift = lse[bh] + __logf(m) - (M + __logf(L));
+    const float shift = lse_prev + __logf(m) - (M + __logf(L));
 #pragma unroll
     for (int e = 0; e < kPre; ++e)
         if (jv[e] >= 0 && jv[e] < ld) srow[jv[e]] = sv[e] + shift;
