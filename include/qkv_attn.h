@@ -168,7 +168,8 @@ int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, const
 /*
  * select_columns - top-k columns of each (sequence, head) under the distribution
  * exp(scores - lse) [project page STEP 02; PyPI Configuration: 10% key retention].
- *   Order: fp32 score descending, ties to the lower index (+0 and -0 are equal).
+ *   Order: fp32 score descending, ties to the lower index (+0 and -0 are equal).  Scores
+ *   should not be NaN; a NaN orders by its bit pattern (a positive NaN above +inf).
  *   0 <= k <= n (k == n takes every column); n <= ld_scores.  Writes k entries per
  *   (sequence, head):
  *   idx    device int32 [batch][heads][k]: selected columns, ascending.
