@@ -263,86 +263,79 @@ __device__ __forceinline__ void axpy32_fp8(const uint4 w, float wt, float* acc) 
     }
 }
 
-// Merge of split-softmax partials of one (sequence, head), laid out as nsplit records of
-// `stride` floats: [max, sum, a[0..D), (b[0..D))].  Thread t owns channel t % D and the
-// records s = t / D (mod NT / D); it loads all of its records' fields first (one memory
-// latency), then the global max, the rescale weights and the sums are formed, and the
-// per-thread sums are added in record-group order (deterministic).  Returns
-// L = sum_s sum_s * exp(max_s - M) and M in *gmax; writes a[c] (rescaled) and, if has_b,
-// b[c] (plain sums) into out_a / out_b (LDS), valid for every thread after the call.
-template <int D, int NT, int NPER>
-__device__ __forceinline__ float merge_partials(const float* pp, int nsplit, int stride, bool has_b, float* red,
-                                                float* out_a, float* out_b, float* grp /* [NT] */, float* gmax) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    constexpr int NW = NT / 64;
-    constexpr int G = NT / D;
-    const int c = tid % D, g = tid / D;
-    float mv[NPER], lv[NPER], av[NPER], bv[NPER];
-#pragma unroll
-    for (int e = 0; e < NPER; ++e) {
-        const int s = g + e * G;
-        mv[e] = -__builtin_huge_valf();
-        lv[e] = av[e] = bv[e] = 0.f;
-        if (s < nsplit) {
-            const float* q = pp + (size_t)s * stride;
-            mv[e] = q[0];
-            lv[e] = q[1];
-            av[e] = q[2 + c];
-            if (has_b) bv[e] = q[2 + D + c];
-        }
+// Merge of split-softmax partials of one (sequence, head), laid out as n records of
+// `stride` floats: [max, sum, a[0..D), (b[0..D) if HAS_B)], by NW waves.
+// Every wave forms the global max M and L = sum_s sum_s * exp(max_s - M) itself: lanes
+// over records, then fixed-order wave reductions, so all waves hold the same M and L and
+// need no barrier for them.  Wave w then adds up records w, w + NW, w + 2 NW, ... in record
+// order (a rescaled by exp(max_s - M), b plain), U records in flight, and leaves its sums in
+// red[w * RS + c] (a) and red[w * RS + D + c] (b), RS = (HAS_B ? 2 : 1) * D.  The caller
+// adds the NW wave sums in wave order after a barrier.
+template <int D, int NW, int U, bool HAS_B>
+__device__ __forceinline__ void merge_records(const float* pp, int n, int stride, float* red, float* gmax,
+                                              float* gsum) {
+    constexpr float kNeg = -__builtin_huge_valf();
+    constexpr int CPL = D / 64;  // channels per lane
+    constexpr int RS = (HAS_B ? 2 : 1) * D;
+    static_assert(CPL == 1 || CPL == 2, "head_dim 64 or 128");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float m0 = lane < n ? pp[(size_t)lane * stride] : kNeg;
+    const float l0 = lane < n ? pp[(size_t)lane * stride + 1] : 0.f;
+    const float m1 = lane + 64 < n ? pp[(size_t)(lane + 64) * stride] : kNeg;
+    const float l1 = lane + 64 < n ? pp[(size_t)(lane + 64) * stride + 1] : 0.f;
+    float m = fmaxf(m0, m1);
+    for (int s = lane + 128; s < n; s += 64) m = fmaxf(m, pp[(size_t)s * stride]);
+    const float M = wave_max(m);
+    float l = 0.f;
+    if (m0 != kNeg) l = l0 * __expf(m0 - M);
+    if (m1 != kNeg) l = fmaf(l1, __expf(m1 - M), l);
+    for (int s = lane + 128; s < n; s += 64) {
+        const float ms = pp[(size_t)s * stride];
+        if (ms != kNeg) l = fmaf(pp[(size_t)s * stride + 1], __expf(ms - M), l);
     }
-    float m = -__builtin_huge_valf();
-#pragma unroll
-    for (int e = 0; e < NPER; ++e) m = fmaxf(m, mv[e]);
-    for (int s = g + NPER * G; s < nsplit; s += G) m = fmaxf(m, pp[(size_t)s * stride]);
-    m = wave_max(m);
-    if (lane == 0) red[wave] = m;
-    __syncthreads();
-    float M = red[0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
     *gmax = M;
-    float a = 0.f, b = 0.f, l = 0.f;
+    *gsum = wave_sum(l);
+
+    float a[CPL], b[CPL];
 #pragma unroll
-    for (int e = 0; e < NPER; ++e) {
-        const float w = (mv[e] == -__builtin_huge_valf()) ? 0.f : __expf(mv[e] - M);
-        a = fmaf(av[e], w, a);
-        l = fmaf(lv[e], w, l);
-        b += bv[e];
-    }
-    for (int s = g + NPER * G; s < nsplit; s += G) {
-        const float* q = pp + (size_t)s * stride;
-        const float w = (q[0] == -__builtin_huge_valf()) ? 0.f : __expf(q[0] - M);
-        a = fmaf(q[2 + c], w, a);
-        l = fmaf(q[1], w, l);
-        if (has_b) b += q[2 + D + c];
-    }
-    __syncthreads();
-    grp[tid] = a;
-    if (c == 0) red[g] = l;
-    __syncthreads();
-    float L = 0.f;
+    for (int i = 0; i < CPL; ++i) a[i] = b[i] = 0.f;
+    for (int s0 = wave; s0 < n; s0 += U * NW) {
+        float ms[U], av[U][CPL], bv[U][CPL];
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) L += red[gg];
-    if (tid < D) {
-        float t = 0.f;
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * NW;
+            const float* r = pp + (size_t)(s < n ? s : n - 1) * stride;  // in range; weighted 0 if s >= n
+            ms[u] = s < n ? r[0] : kNeg;
+            if (CPL == 2) {
+                const float2 x = *reinterpret_cast<const float2*>(r + 2 + 2 * lane);
+                av[u][0] = x.x;
+                av[u][CPL - 1] = x.y;
+                if (HAS_B) {
+                    const float2 y = *reinterpret_cast<const float2*>(r + 2 + D + 2 * lane);
+                    bv[u][0] = y.x;
+                    bv[u][CPL - 1] = y.y;
+                }
+            } else {
+                av[u][0] = r[2 + lane];
+                if (HAS_B) bv[u][0] = r[2 + D + lane];
+            }
+        }
 #pragma unroll
-        for (int gg = 0; gg < G; ++gg) t += grp[gg * D + tid];
-        out_a[tid] = t;
-    }
-    if (has_b) {
-        __syncthreads();
-        grp[tid] = b;
-        __syncthreads();
-        if (tid < D) {
-            float t = 0.f;
+        for (int u = 0; u < U; ++u) {
+            const float w = ms[u] == kNeg ? 0.f : __expf(ms[u] - M);
 #pragma unroll
-            for (int gg = 0; gg < G; ++gg) t += grp[gg * D + tid];
-            out_b[tid] = t;
+            for (int i = 0; i < CPL; ++i) a[i] = fmaf(av[u][i], w, a[i]);
+            if (HAS_B && s0 + u * NW < n) {
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) b[i] += bv[u][i];
+            }
         }
     }
-    __syncthreads();
-    return L;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        red[wave * RS + CPL * lane + i] = a[i];
+        if (HAS_B) red[wave * RS + D + CPL * lane + i] = b[i];
+    }
 }
 
 }  // namespace qkv

@@ -425,22 +425,23 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
 // Second kernel of the reader: merges the splits of each (sequence, head) in split order.
 // (A kernel boundary publishes the partials; a per-workgroup device-scope fence in the
 // split kernel would write back and invalidate L2 once per workgroup.)
-constexpr int kCombineThreads = 1024;
+constexpr int kCombineWaves = 8;
 
 template <int D>
-__global__ __launch_bounds__(kCombineThreads) void dense_combine_kernel(const float* __restrict__ part, int nsplit1,
-                                                                        uint16_t* __restrict__ o,
-                                                                        float* __restrict__ o32,
-                                                                        float* __restrict__ lse) {
+__global__ __launch_bounds__(64 * kCombineWaves) void dense_combine_kernel(const float* __restrict__ part, int nsplit,
+                                                                          uint16_t* __restrict__ o,
+                                                                          float* __restrict__ o32,
+                                                                          float* __restrict__ lse) {
     const int bh = blockIdx.x, tid = threadIdx.x;
-    __shared__ float red[kCombineThreads / 64];
-    __shared__ float oa[D];
-    __shared__ float grp[kCombineThreads];
-    const float* pp = part + (size_t)bh * nsplit1 * (D + 2);
-    float M;
-    const float L = merge_partials<D, kCombineThreads, 12>(pp, nsplit1, D + 2, false, red, oa, nullptr, grp, &M);
+    __shared__ float red[kCombineWaves * D];
+    float M, L;
+    merge_records<D, kCombineWaves, 8, false>(part + (size_t)bh * nsplit * (D + 2), nsplit, D + 2, red, &M, &L);
+    __syncthreads();
     if (tid < D) {
-        const float oc = oa[tid] / L;
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < kCombineWaves; ++w) t += red[w * D + tid];
+        const float oc = t / L;
         o32[(size_t)bh * D + tid] = oc;
         if (o) o[(size_t)bh * D + tid] = f32_to_bf16_rne(oc);
     }
@@ -484,7 +485,7 @@ static void launch_dense_d(const CacheArg& ca, int loop, const uint16_t* q, NewR
         dense_split_kernel<D, 2><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit, pl.spb);
     else
         dense_split_kernel<D, 1><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit, pl.spb);
-    dense_combine_kernel<D><<<ca.B * ca.H, kCombineThreads, 0, st>>>(part, pl.nsplit, o, o32, lse);
+    dense_combine_kernel<D><<<ca.B * ca.H, 64 * kCombineWaves, 0, st>>>(part, pl.nsplit, o, o32, lse);
 }
 
 int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, uint16_t* o, float* o32,

@@ -26,6 +26,8 @@ constexpr int kWaveRounds = 3;                 // column rounds per wave
 // selected columns per workgroup (4 waves): d/8 lanes per column, 64 / (d/8) per round
 constexpr int kSpWaves = 4;                    // waves per workgroup
 constexpr int chunk_cols(int D) { return kSpWaves * kWaveRounds * (64 / (D / 8)); }
+// A chunk's partial record: [max, sum, -, -, U[0..D), W[0..D)], 16-byte aligned.
+constexpr int sp_record(int D) { return 2 * D + 4; }
 
 __device__ __forceinline__ void codes8(uint32_t w, float* c) {
 #pragma unroll
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(64 * kSpWaves) void sparse_chunk_kernel(CacheArg ca
     float M = wm[0];
 #pragma unroll
     for (int w = 1; w < kSpWaves; ++w) M = fmaxf(M, wm[w]);
-    float* out = part + ((size_t)bh * gridDim.x + chunk) * (2 + 2 * D);
+    float* out = part + ((size_t)bh * gridDim.x + chunk) * sp_record(D);
     for (int t = tid; t < 2 * D; t += 64 * kSpWaves) {
         float a = 0.f;
         if (t < D) {
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(64 * kSpWaves) void sparse_chunk_kernel(CacheArg ca
 #pragma unroll
             for (int w = 0; w < kSpWaves; ++w) a += wW[w][t - D];
         }
-        out[2 + t] = a;
+        out[4 + t] = a;
     }
     if (tid == 0) {
         float L = 0.f;
@@ -214,19 +216,77 @@ __global__ __launch_bounds__(64 * kSpWaves) void sparse_chunk_kernel(CacheArg ca
 
 // Merges the chunk partials of each (sequence, head): o = o_prev + m * U / L - W, then
 // shifts the selected scores onto the previous lse scale.
-constexpr int kSpCombineThreads = 1024;
+constexpr int kSpCombineWaves = 16;
+
+// Merge of the n chunk records of one (sequence, head) by NW waves.  Every wave forms the
+// global max M and L = sum_s sum_s * exp(max_s - M) itself (lanes over records, fixed-order
+// wave reductions).  Wave w then adds up records w, w + NW, ... in record order, U in
+// flight: one 16-byte load per lane and record, lanes [0, D/4) holding U (rescaled by
+// exp(max_s - M)) and lanes [D/4, D/2) holding W (plain sums).  Its sums go to
+// red[w * 2D + c] (U) and red[w * 2D + D + c] (W); the caller adds the NW wave sums in wave
+// order after a barrier.
+template <int D, int NW, int U>
+__device__ __forceinline__ void merge_chunk_records(const float* pp, int n, float* red, float* gmax, float* gsum) {
+    constexpr float kNeg = -__builtin_huge_valf();
+    constexpr int SR = sp_record(D);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const float m0 = lane < n ? pp[(size_t)lane * SR] : kNeg;
+    const float l0 = lane < n ? pp[(size_t)lane * SR + 1] : 0.f;
+    const float m1 = lane + 64 < n ? pp[(size_t)(lane + 64) * SR] : kNeg;
+    const float l1 = lane + 64 < n ? pp[(size_t)(lane + 64) * SR + 1] : 0.f;
+    float m = fmaxf(m0, m1);
+    for (int s = lane + 128; s < n; s += 64) m = fmaxf(m, pp[(size_t)s * SR]);
+    const float M = wave_max(m);
+    float l = 0.f;
+    if (m0 != kNeg) l = l0 * __expf(m0 - M);
+    if (m1 != kNeg) l = fmaf(l1, __expf(m1 - M), l);
+    for (int s = lane + 128; s < n; s += 64) {
+        const float ms = pp[(size_t)s * SR];
+        if (ms != kNeg) l = fmaf(pp[(size_t)s * SR + 1], __expf(ms - M), l);
+    }
+    *gmax = M;
+    *gsum = wave_sum(l);
+
+    const bool on = lane < D / 2, is_u = lane < D / 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = wave; s0 < n; s0 += U * NW) {
+        float4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * NW;
+            x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (s < n && on) x[u] = reinterpret_cast<const float4*>(pp + (size_t)s * SR)[1 + lane];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * NW;
+            if (s < n) {
+                const int mb = s < 64 ? __builtin_amdgcn_readlane(__float_as_int(m0), s)
+                                      : s < 128 ? __builtin_amdgcn_readlane(__float_as_int(m1), s - 64)
+                                                : __float_as_int(pp[(size_t)s * SR]);
+                const float msf = __int_as_float(mb);
+                const float w = is_u ? (msf == kNeg ? 0.f : __expf(msf - M)) : 1.f;
+                acc.x = fmaf(x[u].x, w, acc.x);
+                acc.y = fmaf(x[u].y, w, acc.y);
+                acc.z = fmaf(x[u].z, w, acc.z);
+                acc.w = fmaf(x[u].w, w, acc.w);
+            }
+        }
+    }
+    if (on) *reinterpret_cast<float4*>(red + wave * 2 * D + 4 * lane) = acc;
+}
 
 template <int D>
-__global__ __launch_bounds__(kSpCombineThreads) void sparse_combine_kernel(
+__global__ __launch_bounds__(64 * kSpCombineWaves) void sparse_combine_kernel(
     const float* __restrict__ part, int nchunk, const float* __restrict__ mass, const float* o_prev,
     const float* __restrict__ lse, const int32_t* __restrict__ idx, const float* __restrict__ cs, int k,
     float* __restrict__ scores, int ld, uint16_t* __restrict__ o, float* o32) {
+    constexpr int NT = 64 * kSpCombineWaves;
     const int bh = blockIdx.x, tid = threadIdx.x;
-    __shared__ float red[kSpCombineThreads / 64];
-    __shared__ float ua[D], wb[D];
-    __shared__ float grp[kSpCombineThreads];
-    const float* pp = part + (size_t)bh * nchunk * (2 + 2 * D);
-    // the selected columns and their raw scores (entry order), read alongside the partials
+    __shared__ __align__(16) float red[kSpCombineWaves * 2 * D];
+    // the selected columns and their raw scores (entry order), the mass, the previous lse
+    // and output: none depends on the merge, so all go out with the partials
     constexpr int kPre = 4;
     float* srow = scores + (size_t)bh * ld;
     const int32_t* id = idx + (size_t)bh * k;
@@ -235,27 +295,34 @@ __global__ __launch_bounds__(kSpCombineThreads) void sparse_combine_kernel(
     float sv[kPre];
 #pragma unroll
     for (int e = 0; e < kPre; ++e) {
-        const int i = tid + e * kSpCombineThreads;
+        const int i = tid + e * NT;
         jv[e] = i < k ? id[i] : -1;
         sv[e] = i < k ? cr[i] : 0.f;
     }
-    // loads that do not depend on the merge go out with it
     const float m = mass[bh], lse_prev = lse[bh];
     const float op = tid < D ? o_prev[(size_t)bh * D + tid] : 0.f;
-    float M;
-    const float L = merge_partials<D, kSpCombineThreads, 12>(pp, nchunk, 2 + 2 * D, true, red, ua, wb, grp, &M);
-    if (tid < D) {
-        const float oc = op + m * (ua[tid] / L) - wb[tid];
-        o32[(size_t)bh * D + tid] = oc;
-        if (o) o[(size_t)bh * D + tid] = f32_to_bf16_rne(oc);
-    }
+    float M, L;
+    merge_chunk_records<D, kSpCombineWaves, 6>(part + (size_t)bh * nchunk * sp_record(D), nchunk, red, &M, &L);
+    // every wave holds M and L: the spliced scores need no barrier
     const float shift = lse_prev + __logf(m) - (M + __logf(L));
 #pragma unroll
     for (int e = 0; e < kPre; ++e)
         if (jv[e] >= 0 && jv[e] < ld) srow[jv[e]] = sv[e] + shift;
-    for (int i = tid + kPre * kSpCombineThreads; i < k; i += kSpCombineThreads) {
+    for (int i = tid + kPre * NT; i < k; i += NT) {
         const int j = id[i];
         if (j >= 0 && j < ld) srow[j] = cr[i] + shift;
+    }
+    __syncthreads();
+    if (tid < D) {
+        float u = 0.f, w = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < kSpCombineWaves; ++wv) {
+            u += red[wv * 2 * D + tid];
+            w += red[wv * 2 * D + D + tid];
+        }
+        const float oc = op + m * (u / L) - w;
+        o32[(size_t)bh * D + tid] = oc;
+        if (o) o[(size_t)bh * D + tid] = f32_to_bf16_rne(oc);
     }
 }
 
@@ -273,7 +340,7 @@ __global__ __launch_bounds__(D) void sparse_copy_kernel(const float* o_prev, uin
 // workspace: chunk partials [B][H][nchunk][2 + 2D], then the raw selected scores [B][H][k]
 size_t sparse_ws_bytes(int B, int H, int D, int k) {
     const int nchunk = (k + chunk_cols(D) - 1) / chunk_cols(D);
-    return (size_t)B * H * nchunk * (2 + 2 * D) * sizeof(float) + (size_t)B * H * k * sizeof(float);
+    return (size_t)B * H * nchunk * sp_record(D) * sizeof(float) + (size_t)B * H * k * sizeof(float);
 }
 
 int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, const int32_t* idx,
@@ -291,15 +358,15 @@ int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow
         return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
     }
     float* part = static_cast<float*>(ws);
-    float* cs = part + (size_t)ca.B * ca.H * nchunk * (2 + 2 * D);
+    float* cs = part + (size_t)ca.B * ca.H * nchunk * sp_record(D);
     dim3 grid(nchunk, ca.H, ca.B);
     if (D == 128) {
         sparse_chunk_kernel<128><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
-        sparse_combine_kernel<128><<<ca.B * ca.H, kSpCombineThreads, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
+        sparse_combine_kernel<128><<<ca.B * ca.H, 64 * kSpCombineWaves, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
                                                                               scores, ld, o, o32);
     } else {
         sparse_chunk_kernel<64><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
-        sparse_combine_kernel<64><<<ca.B * ca.H, kSpCombineThreads, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
+        sparse_combine_kernel<64><<<ca.B * ca.H, 64 * kSpCombineWaves, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
                                                                              scores, ld, o, o32);
     }
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
