@@ -122,6 +122,22 @@ __device__ __forceinline__ float wave_sum(float v) {
     return add_xor32(v);
 }
 
+// Sets the wave's instruction issue priority (s_setprio, 0..3) from the share of its work
+// still left: a wave with more left is preferred.  The arbiter otherwise prefers the oldest
+// wave, so workgroups sharing a CU would run one after another.
+__device__ __forceinline__ void prio_by_work_left(int left, int total) {
+    int lv = total > 0 ? (4 * left) / total : 0;
+    lv = __builtin_amdgcn_readfirstlane(lv > 3 ? 3 : lv);
+    if (lv == 3)
+        __builtin_amdgcn_s_setprio(3);
+    else if (lv == 2)
+        __builtin_amdgcn_s_setprio(2);
+    else if (lv == 1)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
+}
+
 // Eight bf16 values (16 bytes) to floats.
 __device__ __forceinline__ void bf16x8(const uint4 w, float* f) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};

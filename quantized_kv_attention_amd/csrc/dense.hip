@@ -209,9 +209,15 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
         }
         __syncthreads();
 
-        // K pass, prepared planes: logits of every row of the block summed over the planes
+        // K pass, prepared planes: logits of every row of the block summed over the planes.
+        // Each block step sets the wave's issue priority from the share of its blocks still
+        // to go (both passes): co-resident workgroups then keep pace with each other, where
+        // oldest-first issue would finish them one after another and leave the CU with a
+        // single workgroup's loads in flight at the end.
+        const int nbw = blkA < blk1 ? (blk1 - blkA + 3) >> 2 : 0;  // this wave's blocks
         for (int blk = blkA; blk < blk1; blk += 4) {
             const int bb = blk - blk0;
+            prio_by_work_left(2 * nbw - ((blk - blkA) >> 2), 2 * nbw);
             if (blk != blkA) load_k(blk);
             float lg[NLD];
 #pragma unroll
@@ -321,6 +327,7 @@ __global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int lo
         // V pass, prepared planes: every plane's codes of the block loaded together
         for (int blk = blkA; blk < blk1; blk += 4) {
             const int bb = blk - blk0;
+            prio_by_work_left(nbw - ((blk - blkA) >> 2), 2 * nbw);
             if (blk != blkA) load_v(blk);
 #pragma unroll
             for (int it = 0; it < NLD; ++it) {
