@@ -97,9 +97,10 @@ __device__ __forceinline__ void vpass_block(const uint8_t* bp, int prt, int rsub
 
 // NPRE (1 or 2): leading dense planes whose blocks are read together, with their folded
 // queries prepared once per split; later planes (sparse, or dense beyond NPRE) follow one
-// by one.
+// by one.  Three waves per SIMD (the plan's three workgroups per CU) leave up to 168 VGPRs
+// per wave: the two-plane kernel needs ~154, and under a 128 cap it spilled to scratch.
 template <int D, int NPRE>
-__global__ __launch_bounds__(256, 4) void dense_split_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                           NewRow nr, float sm, float* __restrict__ scores, int ld,
                                                           float* __restrict__ part, int nsplit, int spb) {
     constexpr int LPR = Block<D>::kLpr, RPI = Block<D>::kRpi, NLD = 64 / RPI;
@@ -463,7 +464,7 @@ DensePlan dense_plan(int B, int H, int n_body) {
         pl.nsplit = 1;  // the tail alone
         return pl;
     }
-    // Splits for about 3 workgroups per CU (768 over 256 CUs, less than the 4 that fit):
+    // Splits for 3 workgroups per CU (768 over 256 CUs; the split kernel's launch bounds fit 3):
     // measured at 32K context, this beats both one full round (1024) and several rounds.
     // More than kMaxSpb - 2 blocks per split would leave no LDS for the tail.
     const long slots = 768;
