@@ -7,13 +7,13 @@
 // (up to 40 of them) in registers.  A histogram over 2048 equal-width value bins between
 // the smallest and largest score finds the bin holding the k-th column (bins are a monotone
 // function of the score, so every bin above it is taken whole); the few columns of that
-// bin are ranked exactly as 64-bit (key, index) words, which gives the threshold (score,
-// index).  A column is then taken iff it is above the threshold in that order; one scan over
-// per-(row, wave) counts places the selected columns in ascending index order.
+// bin are ranked exactly as 64-bit (key, index) words, which gives the threshold score.  When
+// no other column has that score, a column is taken iff its score is at least the threshold;
+// one scan over per-(row, wave) counts places the selected columns in ascending index order.
 //
 // The fast path is kept small (its unrolled loops carry no mode branches).  Everything
-// else (k >= n, equal, infinite or NaN scores, a crowded threshold bin, contexts beyond
-// 40960 columns) goes to plain loops over memory: a 3-pass radix threshold on an
+// else (k >= n, equal, infinite or NaN scores, a crowded threshold bin, a threshold score
+// that other columns share, contexts beyond 40960 columns) goes to plain loops over memory: a 3-pass radix threshold on an
 // order-preserving integer key and a row-by-row compaction.
 #include "launch.h"
 
@@ -42,10 +42,11 @@ __device__ __forceinline__ uint64_t sort_word(float x, int j) {
     return ((uint64_t)order_key(x) << 32) | (uint64_t)(~(uint32_t)j);
 }
 
-__device__ __forceinline__ uint32_t value_bin(float x, float lo, float scale) {
+// Bin of a score x >= lo in [0, kBins); -inf (a column past n) gets bin -1.
+__device__ __forceinline__ int value_bin(float x, float lo, float scale) {
     float f = (x - lo) * scale;
-    f = fminf(fmaxf(f, 0.f), (float)(kBins - 1));
-    return (uint32_t)(int)f;
+    f = fminf(fmaxf(f, -1.f), (float)(kBins - 1));
+    return (int)f;
 }
 
 __device__ __forceinline__ uint64_t lanes_below() {
@@ -53,16 +54,23 @@ __device__ __forceinline__ uint64_t lanes_below() {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Inclusive prefix sum over the wave: row shifts by 1, 2, 4 and 8 (a lane whose source is
+// outside its 16-lane row adds 0), then each row's last lane carried into the rows after it.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
 // Exclusive prefix sum over the workgroup (one barrier); *total = sum over all threads.
 // sh (kSelWaves words) may be reused after the caller's next barrier.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_up(x, o, 64);
-        if (lane >= o) x += t;
-    }
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t x = wave_incl_scan(v);
     if (lane == 63) sh[wave] = x;
     __syncthreads();
     uint32_t before = 0, all = 0;
@@ -175,6 +183,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
     __shared__ uint32_t bcast[4];
     __shared__ uint64_t cand[kCandCap];
     __shared__ uint64_t thr_sh;
+    __shared__ uint32_t thr_unique;
     __shared__ uint32_t row_off[kSelPerThread * kSelWaves];  // [row][wave]: counts, then offsets
     __shared__ int32_t st_idx[kStage];
     __shared__ float st_p[kStage];
@@ -190,14 +199,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
     bool done = false;  // uniform
 
     if (k < n && E <= kSelPerThread) {
-        // ---- fast path: column j = e * 1024 + tid in v[e] (columns past n repeat column n-1,
-        //      which leaves the extremes unchanged; every later use tests j < n) ----
+        // ---- fast path: column j = e * 1024 + tid in v[e]; the slots past n first hold
+        //      copies of column n - 1 (no change to the extremes), then -inf, which no bin
+        //      counts and no threshold takes ----
+        const float kNegInf = -__builtin_huge_valf();
         float v[kSelPerThread];
 #pragma unroll
         for (int e = 0; e < kSelPerThread; ++e) v[e] = sc[min(e * kSelThreads + tid, n - 1)];
         for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
         for (int i = tid; i < kCandCap; i += kSelThreads) cand[i] = 0;  // padding ranks below everything
-        float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+        float mn = __builtin_huge_valf(), mx = kNegInf;
         uint64_t nan_lanes = 0;
 #pragma unroll
         for (int e = 0; e < kSelPerThread; ++e) {
@@ -213,6 +224,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
             fmax_sh[wave] = mx;
         }
         if (tid == 0) bcast[2] = 0;  // candidate count
+#pragma unroll
+        for (int e = 0; e < kSelPerThread; ++e) v[e] = e * kSelThreads + tid < n ? v[e] : kNegInf;
         __syncthreads();
         float lo = fmin_sh[0], hi = fmax_sh[0];
 #pragma unroll
@@ -225,101 +238,112 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
         if (range > 0.f && __builtin_isfinite(range) && __builtin_isfinite(scale)) {
 #pragma unroll
             for (int e = 0; e < kSelPerThread; ++e)
-                if (e * kSelThreads + tid < n) atomicAdd(&hist[value_bin(v[e], lo, scale)], 1u);
+                if (v[e] > kNegInf) atomicAdd(&hist[value_bin(v[e], lo, scale)], 1u);
             __syncthreads();
             // bin of the k-th largest, counting from the top bin (thread t: bins 2047-2t, 2046-2t)
-            const uint32_t b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
+            const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
             const uint32_t c0 = hist[b0], c1 = hist[b1];
             uint32_t tot;
             const uint32_t above = block_excl_scan(c0 + c1, scan_sh, &tot);
             if (above < (uint32_t)k && (uint32_t)k <= above + c0) {
-                bcast[0] = b0;
+                bcast[0] = (uint32_t)b0;
                 bcast[1] = above;
             } else if (above + c0 < (uint32_t)k && (uint32_t)k <= above + c0 + c1) {
-                bcast[0] = b1;
+                bcast[0] = (uint32_t)b1;
                 bcast[1] = above + c0;
             }
             __syncthreads();
-            const uint32_t bstar = bcast[0];
+            const int bstar = (int)bcast[0];
             const uint32_t need_in = (uint32_t)k - bcast[1];  // columns taken inside the threshold bin
             if (hist[bstar] <= (uint32_t)kCandCap) {
                 // the threshold bin's columns as (key, index) sort words
 #pragma unroll
                 for (int e = 0; e < kSelPerThread; ++e) {
-                    const int j = e * kSelThreads + tid;
-                    if (j < n && value_bin(v[e], lo, scale) == bstar) {
+                    if (value_bin(v[e], lo, scale) == bstar) {  // never for -inf (bin -1)
                         const uint32_t slot = atomicAdd(&bcast[2], 1u);
-                        cand[slot] = sort_word(v[e], j);
+                        cand[slot] = sort_word(v[e], e * kSelThreads + tid);
                     }
                 }
                 __syncthreads();
                 // the candidate of rank need_in - 1 (bins are monotone in the score, so every
-                // column of a higher bin precedes it and every column of a lower bin follows)
+                // column of a higher bin precedes it and every column of a lower bin follows),
+                // and whether any other column has its score
                 const uint32_t c = bcast[2];
                 const uint32_t cpad = (c + 7u) & ~7u;
                 for (uint32_t t = tid; t < c; t += kSelThreads) {
                     const uint64_t rt = cand[t];
-                    uint32_t rank = 0;
+                    const uint32_t kt = (uint32_t)(rt >> 32);
+                    uint32_t rank = 0, same = 0;
                     for (uint32_t u = 0; u < cpad; u += 8) {
 #pragma unroll
-                        for (int w = 0; w < 8; ++w) rank += cand[u + w] > rt ? 1u : 0u;
-                    }
-                    if (rank == need_in - 1) thr_sh = rt;
-                }
-                __syncthreads();
-                const uint64_t thr = thr_sh;
-                const float tx = key_float((uint32_t)(thr >> 32));
-                const int ti = (int)~(uint32_t)thr;
-                // taken <=> score above tx, or equal to it at an index <= ti
-                // per-(row, wave) counts (lane e of cnts: row e), one scan, then each position
-                uint32_t cnts = 0;
-#pragma unroll
-                for (int e = 0; e < kSelPerThread; ++e) {
-                    const int j = e * kSelThreads + tid;
-                    const bool f = (v[e] > tx && j < n) || (v[e] == tx && j <= ti);
-                    const uint32_t cnt = (uint32_t)__popcll(__ballot(f));
-                    cnts = lane == e ? cnt : cnts;
-                }
-                if (lane < E) row_off[lane * kSelWaves + wave] = cnts;
-                __syncthreads();
-                const int nrw = E * kSelWaves;
-                uint32_t tot2;
-                const uint32_t x = tid < nrw ? row_off[tid] : 0u;
-                const uint32_t ex = block_excl_scan(x, scan_sh, &tot2);
-                __syncthreads();  // every count has been read
-                if (tid < nrw) row_off[tid] = ex;
-                __syncthreads();
-                const uint32_t offs = lane < E ? row_off[lane * kSelWaves + wave] : 0u;
-                const bool stage = k <= kStage;
-#pragma unroll
-                for (int e = 0; e < kSelPerThread; ++e) {
-                    const int j = e * kSelThreads + tid;
-                    const bool f = (v[e] > tx && j < n) || (v[e] == tx && j <= ti);
-                    const uint64_t bal = __ballot(f);
-                    const uint32_t base = __builtin_amdgcn_readlane(offs, e);
-                    if (f) {
-                        const uint32_t pos =
-                            base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-                        const float p = __expf(v[e] - l);
-                        psum += p;
-                        if (stage) {
-                            st_idx[pos] = j;
-                            st_p[pos] = p;
-                        } else {
-                            id[pos] = j;
-                            ps[pos] = p;
+                        for (int w = 0; w < 8; ++w) {
+                            const uint64_t cu = cand[u + w];
+                            rank += cu > rt ? 1u : 0u;
+                            same += (uint32_t)(cu >> 32) == kt ? 1u : 0u;
                         }
                     }
-                }
-                if (stage) {
-                    __syncthreads();
-                    for (int i = tid; i < k; i += kSelThreads) {
-                        id[i] = st_idx[i];
-                        ps[i] = st_p[i];
+                    if (rank == need_in - 1) {
+                        thr_sh = rt;
+                        thr_unique = same == 1u;
                     }
                 }
-                done = true;
+                __syncthreads();
+                if (thr_unique) {
+                    // a unique threshold score tx: a column is taken iff its score is >= tx
+                    // (columns past n hold -inf); per-(row, wave) counts (lane e of cnts: row
+                    // e), one scan, then each column's position
+                    const float tx = key_float((uint32_t)(thr_sh >> 32));
+                    uint32_t cnts = 0;
+#pragma unroll
+                    for (int e = 0; e < kSelPerThread; ++e) {
+                        const uint32_t cnt = (uint32_t)__popcll(__ballot(v[e] >= tx));
+                        cnts = lane == e ? cnt : cnts;
+                    }
+                    if (lane < E) row_off[lane * kSelWaves + wave] = cnts;
+                    __syncthreads();
+                    const int nrw = E * kSelWaves;
+                    uint32_t tot2;
+                    const uint32_t x = tid < nrw ? row_off[tid] : 0u;
+                    const uint32_t ex = block_excl_scan(x, scan_sh, &tot2);
+                    __syncthreads();  // every count has been read
+                    if (tid < nrw) row_off[tid] = ex;
+                    __syncthreads();
+                    const uint32_t offs = lane < E ? row_off[lane * kSelWaves + wave] : 0u;
+                    const bool stage = k <= kStage;
+                    // the comparisons are made again below rather than kept across the scan
+                    // (40 lane masks would not fit in scalar registers)
+                    float txp = tx;
+                    asm volatile("" : "+v"(txp));
+#pragma unroll
+                    for (int e = 0; e < kSelPerThread; ++e) {
+                        const bool f = v[e] >= txp;
+                        const uint64_t bal = __ballot(f);
+                        const uint32_t base = __builtin_amdgcn_readlane(offs, e);
+                        if (f) {
+                            const uint32_t pos =
+                                base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                            const int j = e * kSelThreads + tid;
+                            const float p = __expf(v[e] - l);
+                            psum += p;
+                            if (stage) {
+                                st_idx[pos] = j;
+                                st_p[pos] = p;
+                            } else {
+                                id[pos] = j;
+                                ps[pos] = p;
+                            }
+                        }
+                    }
+                    if (stage) {
+                        __syncthreads();
+                        for (int i = tid; i < k; i += kSelThreads) {
+                            id[i] = st_idx[i];
+                            ps[i] = st_p[i];
+                        }
+                    }
+                    done = true;
+                }
             }
         }
         __syncthreads();

@@ -56,3 +56,27 @@ def test_ties_and_degenerate(n):
     lse = np.zeros((1, 4), np.float32)
     for k in (1, n // 10, n // 2, n - 1, n):
         run_case(S, lse, k)
+
+
+@pytest.mark.parametrize("n,k", [(4097, 410), (32769, 3277)])
+def test_few_ties_at_and_near_the_threshold(n, k):
+    # spread scores with a handful of copies placed on the k-th largest score (a 2- and a
+    # 3-way tie across the boundary of the selection, decided by index) and just above and
+    # below it while the k-th score itself is unique
+    g = np.random.default_rng(n + k)
+    S = (g.standard_normal((1, 4, n)) * 1.3).astype(np.float32)
+    for h, copies in ((0, 1), (1, 2)):
+        row = S[0, h]
+        order = np.argsort(-row, kind="stable")
+        t = row[order[k - 1]]
+        others = g.choice(np.setdiff1d(np.arange(n), [order[k - 1]]), copies, replace=False)
+        row[others] = t
+    row = S[0, 2]
+    order = np.argsort(-row, kind="stable")
+    row[g.choice(order[k + 5:], 3, replace=False)] = row[order[k - 3]]   # ties above the threshold
+    row[g.choice(order[:k - 5], 3, replace=False)] = row[order[k + 2]]   # ties below it
+    S[0, 3] = np.round(S[0, 3] * 64) / 64                                # many small ties everywhere
+    lse = np.log(np.exp(S.astype(np.float64)).sum(-1)).astype(np.float32)
+    say(f"  select few ties n={n} k={k}")
+    for kk in (k - 1, k, k + 1):
+        run_case(S, lse, kk)
