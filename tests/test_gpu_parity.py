@@ -59,6 +59,18 @@ def test_ragged_d128_multihead():
     check_step(p, p.queries(30), w.n_dense, w.k_cols(p.gpu.n_ctx), "n=1025 d=128 after flush")
 
 
+def test_ragged_d64_several_splits_and_chunks():
+    # head_dim 64 at a ragged length: 12 dense splits and 4 sparse chunks per (b, h), so
+    # both merges combine several records with half-wave rows
+    w = dataclasses.replace(W["tiny"], H=2)
+    p = Pair(w, n=3000, extra=70)
+    compare_planes(p.gpu, p.orc, range(2), range(2))
+    check_step(p, p.queries(0), w.n_dense, w.k_cols(3000), "n=3000 d=64")
+    for step in range(40):
+        p.append(step)
+    check_step(p, p.queries(41), w.n_dense, w.k_cols(p.gpu.n_ctx), "n=3040 d=64 after flush")
+
+
 def test_batch_with_different_masks():
     w = dataclasses.replace(W["batch8"], B=3, H=2)
     p = Pair(w, n=700, extra=8)
