@@ -42,11 +42,10 @@ __device__ __forceinline__ uint64_t sort_word(float x, int j) {
     return ((uint64_t)order_key(x) << 32) | (uint64_t)(~(uint32_t)j);
 }
 
-// Bin of a score x >= lo in [0, kBins); -inf (a column past n) gets bin -1.
-__device__ __forceinline__ int value_bin(float x, float lo, float scale) {
-    float f = (x - lo) * scale;
-    f = fminf(fmaxf(f, -1.f), (float)(kBins - 1));
-    return (int)f;
+// Bin of a score x >= lo in [0, kBins) (off = -lo * scale); -inf (a column past n) gets
+// bin -1.  Monotone in x, which is all the selection needs of it.
+__device__ __forceinline__ int value_bin(float x, float scale, float off) {
+    return (int)__builtin_amdgcn_fmed3f(fmaf(x, scale, off), -1.f, (float)(kBins - 1));
 }
 
 __device__ __forceinline__ uint64_t lanes_below() {
@@ -209,14 +208,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
         for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
         for (int i = tid; i < kCandCap; i += kSelThreads) cand[i] = 0;  // padding ranks below everything
         float mn = __builtin_huge_valf(), mx = kNegInf;
-        uint64_t nan_lanes = 0;
+        float vsum = 0.f;  // NaN iff some score is NaN (or +inf and -inf meet: not finite either)
 #pragma unroll
         for (int e = 0; e < kSelPerThread; ++e) {
             mn = fminf(mn, v[e]);
             mx = fmaxf(mx, v[e]);
-            nan_lanes |= __ballot(__builtin_isnan(v[e]));
+            vsum += v[e];
         }
-        if (nan_lanes) mx = __builtin_huge_valf();  // NaN: the key order of the memory paths decides
+        if (__ballot(__builtin_isnan(vsum))) mx = __builtin_huge_valf();  // the memory paths decide
         mn = wave_min(mn);
         mx = wave_max(mx);
         if (lane == 0) {
@@ -235,10 +234,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
         }
         const float range = hi - lo;
         const float scale = (float)kBins / range;
+        const float boff = -lo * scale;
         if (range > 0.f && __builtin_isfinite(range) && __builtin_isfinite(scale)) {
 #pragma unroll
             for (int e = 0; e < kSelPerThread; ++e)
-                if (v[e] > kNegInf) atomicAdd(&hist[value_bin(v[e], lo, scale)], 1u);
+                if (v[e] > kNegInf) atomicAdd(&hist[value_bin(v[e], scale, boff)], 1u);
             __syncthreads();
             // bin of the k-th largest, counting from the top bin (thread t: bins 2047-2t, 2046-2t)
             const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
                 // the threshold bin's columns as (key, index) sort words
 #pragma unroll
                 for (int e = 0; e < kSelPerThread; ++e) {
-                    if (value_bin(v[e], lo, scale) == bstar) {  // never for -inf (bin -1)
+                    if (value_bin(v[e], scale, boff) == bstar) {  // never for -inf (bin -1)
                         const uint32_t slot = atomicAdd(&bcast[2], 1u);
                         cand[slot] = sort_word(v[e], e * kSelThreads + tid);
                     }
@@ -324,12 +324,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
                                 base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
                             const int j = e * kSelThreads + tid;
-                            const float p = __expf(v[e] - l);
-                            psum += p;
-                            if (stage) {
+                            if (stage) {  // the score; its probability is formed once, below
                                 st_idx[pos] = j;
-                                st_p[pos] = p;
+                                st_p[pos] = v[e];
                             } else {
+                                const float p = __expf(v[e] - l);
+                                psum += p;
                                 id[pos] = j;
                                 ps[pos] = p;
                             }
@@ -338,8 +338,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
                     if (stage) {
                         __syncthreads();
                         for (int i = tid; i < k; i += kSelThreads) {
+                            const float p = __expf(st_p[i] - l);
+                            psum += p;
                             id[i] = st_idx[i];
-                            ps[i] = st_p[i];
+                            ps[i] = p;
                         }
                     }
                     done = true;
