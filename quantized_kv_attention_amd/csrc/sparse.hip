@@ -50,8 +50,14 @@ __device__ __forceinline__ void store_new_row(NewRow nr, uint16_t* tk, uint16_t*
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(64 * kSpWaves) void sparse_chunk_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
+// SB: planes whose slots and data a column loads together.  SB = 1 (chains of up to four
+// planes) keeps the kernel at 92 VGPRs, 5 waves per SIMD.  SB = 4 (deeper chains, whose
+// loads would otherwise be one memory latency per plane) issues a batch's slot lookups
+// together and then every plane's data of the batch together; a plane that does not store
+// the column loads its block 0 and weighs it 0, so every plane must hold a block.  It
+// runs at 3 waves per SIMD (up to 168 VGPRs).
+template <int D, int SB>
+__global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 5) void sparse_chunk_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                            NewRow nr, float sm, const int32_t* __restrict__ idx,
                                                            const float* __restrict__ p_sel, int k,
                                                            float* __restrict__ cs,
@@ -105,40 +111,106 @@ __global__ __launch_bounds__(64 * kSpWaves) void sparse_chunk_kernel(CacheArg ca
             bf16x8(*reinterpret_cast<const uint4*>(ca.tail_v[loop - 2] + off), vh);
         } else {
             bool act_r = false;
-            for (int p = 0; p < loop; ++p) {
-                const PlaneArg& P = ca.p[p];
-                const int slot = P.dense ? j : P.rowmap[(size_t)b * cap + j];
-                if (slot < 0 || slot >= P.n_blocks * 64) continue;
-                const uint8_t* bp = block_ptr<D>(P, ca.H, b, h, slot >> 6);
-                const int row = slot & 63;
-                const uint32_t kw = *reinterpret_cast<const uint32_t*>(bp + Block<D>::kKc + row * (D / 2) + prt * 4);
-                const uint32_t vw = *reinterpret_cast<const uint32_t*>(bp + Block<D>::kVc + row * (D / 2) + prt * 4);
-                const float* km = reinterpret_cast<const float*>(bp + Block<D>::kKm) + c0;
-                const float4 s0 = *reinterpret_cast<const float4*>(km);
-                const float4 s1 = *reinterpret_cast<const float4*>(km + 4);
-                const float4 z0 = *reinterpret_cast<const float4*>(km + D);
-                const float4 z1 = *reinterpret_cast<const float4*>(km + D + 4);
-                const float2 vm = *reinterpret_cast<const float2*>(bp + Block<D>::kVm + (row * (D / 64) + (c0 >> 6)) * 8);
-                const float ks[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-                const float kz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-                float code[8];
-                codes8(kw, code);
+            // the column's slots are looked up SB planes at a time, all in flight together
+            // (they are independent), before any of those planes' data is read
+            for (int p0 = 0; p0 < loop; p0 += SB) {
+                int sl[SB];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const float deq = fmaf(code[c], ks[c], kz[c]);
-                    kh[c] = (p == 0) ? deq : kh[c] + deq;
+                for (int u = 0; u < SB; ++u) {
+                    sl[u] = -1;
+                    if (p0 + u < loop) {
+                        const PlaneArg& P = ca.p[p0 + u];
+                        sl[u] = P.dense ? j : P.rowmap[(size_t)b * cap + j];
+                    }
                 }
-                codes8(vw, code);
-                if (p < loop - 1) {
+                if constexpr (SB > 1) {
+                    uint32_t kw[SB], vw[SB];
+                    float4 s0[SB], s1[SB], z0[SB], z1[SB];
+                    float2 vm[SB];
+                    bool act[SB];
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        const float deq = fmaf(code[c], vm.x, vm.y);
-                        vh[c] = (p == 0) ? deq : vh[c] + deq;
+                    for (int u = 0; u < SB; ++u) {
+                        const int p = min(p0 + u, loop - 1);
+                        const PlaneArg& P = ca.p[p];
+                        act[u] = p0 + u < loop && sl[u] >= 0 && sl[u] < P.n_blocks * 64;
+                        const int slot = act[u] ? sl[u] : 0;
+                        const uint8_t* bp = block_ptr<D>(P, ca.H, b, h, slot >> 6);
+                        const int row = slot & 63;
+                        kw[u] = *reinterpret_cast<const uint32_t*>(bp + Block<D>::kKc + row * (D / 2) + prt * 4);
+                        vw[u] = *reinterpret_cast<const uint32_t*>(bp + Block<D>::kVc + row * (D / 2) + prt * 4);
+                        const float* km = reinterpret_cast<const float*>(bp + Block<D>::kKm) + c0;
+                        s0[u] = *reinterpret_cast<const float4*>(km);
+                        s1[u] = *reinterpret_cast<const float4*>(km + 4);
+                        z0[u] = *reinterpret_cast<const float4*>(km + D);
+                        z1[u] = *reinterpret_cast<const float4*>(km + D + 4);
+                        vm[u] = *reinterpret_cast<const float2*>(bp + Block<D>::kVm + (row * (D / 64) + (c0 >> 6)) * 8);
+                    }
+#pragma unroll
+                    for (int u = 0; u < SB; ++u) {
+                        const int p = p0 + u;
+                        if (!act[u]) continue;
+                        const float ks[8] = {s0[u].x, s0[u].y, s0[u].z, s0[u].w, s1[u].x, s1[u].y, s1[u].z, s1[u].w};
+                        const float kz[8] = {z0[u].x, z0[u].y, z0[u].z, z0[u].w, z1[u].x, z1[u].y, z1[u].z, z1[u].w};
+                        float code[8];
+                        codes8(kw[u], code);
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) {
+                            const float deq = fmaf(code[c], ks[c], kz[c]);
+                            kh[c] = (p == 0) ? deq : kh[c] + deq;
+                        }
+                        codes8(vw[u], code);
+                        if (p < loop - 1) {
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) {
+                                const float deq = fmaf(code[c], vm[u].x, vm[u].y);
+                                vh[c] = (p == 0) ? deq : vh[c] + deq;
+                            }
+                        } else {
+                            act_r = true;
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) vc[c] = vh[c] + fmaf(code[c], vm[u].x, vm[u].y);
+                        }
                     }
                 } else {
-                    act_r = true;
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) vc[c] = vh[c] + fmaf(code[c], vm.x, vm.y);
+                    for (int u = 0; u < SB; ++u) {
+                        const int p = p0 + u;
+                        if (p >= loop) break;
+                        const PlaneArg& P = ca.p[p];
+                        const int slot = sl[u];
+                        if (slot < 0 || slot >= P.n_blocks * 64) continue;
+                        const uint8_t* bp = block_ptr<D>(P, ca.H, b, h, slot >> 6);
+                        const int row = slot & 63;
+                        const uint32_t kw = *reinterpret_cast<const uint32_t*>(bp + Block<D>::kKc + row * (D / 2) + prt * 4);
+                        const uint32_t vw = *reinterpret_cast<const uint32_t*>(bp + Block<D>::kVc + row * (D / 2) + prt * 4);
+                        const float* km = reinterpret_cast<const float*>(bp + Block<D>::kKm) + c0;
+                        const float4 s0 = *reinterpret_cast<const float4*>(km);
+                        const float4 s1 = *reinterpret_cast<const float4*>(km + 4);
+                        const float4 z0 = *reinterpret_cast<const float4*>(km + D);
+                        const float4 z1 = *reinterpret_cast<const float4*>(km + D + 4);
+                        const float2 vm = *reinterpret_cast<const float2*>(bp + Block<D>::kVm + (row * (D / 64) + (c0 >> 6)) * 8);
+                        const float ks[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+                        const float kz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+                        float code[8];
+                        codes8(kw, code);
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) {
+                            const float deq = fmaf(code[c], ks[c], kz[c]);
+                            kh[c] = (p == 0) ? deq : kh[c] + deq;
+                        }
+                        codes8(vw, code);
+                        if (p < loop - 1) {
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) {
+                                const float deq = fmaf(code[c], vm.x, vm.y);
+                                vh[c] = (p == 0) ? deq : vh[c] + deq;
+                            }
+                        } else {
+                            act_r = true;
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) vc[c] = vh[c] + fmaf(code[c], vm.x, vm.y);
+                        }
+                    }
                 }
             }
             if (!act_r) {
@@ -360,12 +432,21 @@ int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow
     float* part = static_cast<float*>(ws);
     float* cs = part + (size_t)ca.B * ca.H * nchunk * sp_record(D);
     dim3 grid(nchunk, ca.H, ca.B);
+    // deep chains: batched loads, which need every plane of the chain to hold a block
+    bool batched = loop > 4;
+    for (int p = 0; batched && p < loop; ++p) batched = ca.p[p].data != nullptr && ca.p[p].n_blocks > 0;
     if (D == 128) {
-        sparse_chunk_kernel<128><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
+        if (!batched)
+            sparse_chunk_kernel<128, 1><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
+        else
+            sparse_chunk_kernel<128, 4><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
         sparse_combine_kernel<128><<<ca.B * ca.H, 64 * kSpCombineWaves, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
                                                                               scores, ld, o, o32);
     } else {
-        sparse_chunk_kernel<64><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
+        if (!batched)
+            sparse_chunk_kernel<64, 1><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
+        else
+            sparse_chunk_kernel<64, 4><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
         sparse_combine_kernel<64><<<ca.B * ca.H, 64 * kSpCombineWaves, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
                                                                              scores, ld, o, o32);
     }
