@@ -51,7 +51,7 @@ __device__ __forceinline__ void store_new_row(NewRow nr, uint16_t* tk, uint16_t*
 }
 
 // SB: planes whose slots and data a column loads together.  SB = 1 (chains of up to four
-// planes) keeps the kernel at 92 VGPRs, 5 waves per SIMD.  SB = 4 (deeper chains, whose
+// planes) keeps the kernel at 92 VGPRs, 5 waves per SIMD.  SB = 3 (deeper chains, whose
 // loads would otherwise be one memory latency per plane) issues a batch's slot lookups
 // together and then every plane's data of the batch together; a plane that does not store
 // the column loads its block 0 and weighs it 0, so every plane must hold a block.  It
@@ -97,8 +97,50 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 5) void sparse_chunk_ke
     const int32_t* id = idx + (size_t)bh * k;
     const float* ps = p_sel + (size_t)bh * k;
 
+    // Deep chains: the chunk's entries whose column the first sparse plane stores (the long
+    // chains) are taken first, spread over the first round of every wave, so that a wave
+    // runs at most one long round while a chunk has no more long columns than a round has
+    // columns over the workgroup.  perm[s] = the entry at sorted position s.
+    __shared__ int perm[SB > 1 ? kChunk : 1];
+    if constexpr (SB > 1) {
+        if (wave == 0) {
+            int probe = -1;  // first sparse plane of the chain (uniform)
+            for (int p = 1; p < loop && probe < 0; ++p)
+                if (!ca.p[p].dense) probe = p;
+            constexpr int NPASS = (kChunk + 63) / 64;
+            const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+            uint64_t lm[NPASS], vm[NPASS];
+            int nlong = 0;
+#pragma unroll
+            for (int t = 0; t < NPASS; ++t) {
+                const int e = t * 64 + lane, i = chunk * kChunk + e;
+                bool lng = false;
+                if (e < kChunk && i < k && probe >= 0) {
+                    const int j = id[i];
+                    if (j >= 0 && j < ca.n_body) lng = ca.p[probe].rowmap[(size_t)b * cap + j] >= 0;
+                }
+                lm[t] = __ballot(lng);
+                vm[t] = __ballot(e < kChunk);
+                nlong += __popcll(lm[t]);
+            }
+            int nl = 0, ns = 0;
+#pragma unroll
+            for (int t = 0; t < NPASS; ++t) {
+                const int e = t * 64 + lane;
+                const bool lng = (lm[t] >> lane) & 1ull;
+                const uint64_t sm_ = ~lm[t] & vm[t];
+                const int s = lng ? nl + __popcll(lm[t] & below) : nlong + ns + __popcll(sm_ & below);
+                if (e < kChunk) perm[s] = e;
+                nl += __popcll(lm[t]);
+                ns += __popcll(sm_);
+            }
+        }
+        __syncthreads();
+    }
+
     for (int round = 0; round < ROUNDS; ++round) {
-        const int i = chunk * kChunk + wave * kWaveCols + round * CPR + cid;
+        const int i = chunk * kChunk + (SB > 1 ? perm[round * (kSpWaves * CPR) + wave * CPR + cid]
+                                               : wave * kWaveCols + round * CPR + cid);
         int j = i < k ? id[i] : 0;
         const bool valid = i < k && j >= 0 && j < ca.n_ctx;
         j = valid ? j : 0;
@@ -432,21 +474,22 @@ int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow
     float* part = static_cast<float*>(ws);
     float* cs = part + (size_t)ca.B * ca.H * nchunk * sp_record(D);
     dim3 grid(nchunk, ca.H, ca.B);
-    // deep chains: batched loads, which need every plane of the chain to hold a block
+    // deep chains: batched loads (and long chains first), which need every plane of the
+    // chain to hold a block
     bool batched = loop > 4;
     for (int p = 0; batched && p < loop; ++p) batched = ca.p[p].data != nullptr && ca.p[p].n_blocks > 0;
     if (D == 128) {
         if (!batched)
             sparse_chunk_kernel<128, 1><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
         else
-            sparse_chunk_kernel<128, 4><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
+            sparse_chunk_kernel<128, 3><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
         sparse_combine_kernel<128><<<ca.B * ca.H, 64 * kSpCombineWaves, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
                                                                               scores, ld, o, o32);
     } else {
         if (!batched)
             sparse_chunk_kernel<64, 1><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
         else
-            sparse_chunk_kernel<64, 4><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
+            sparse_chunk_kernel<64, 3><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
         sparse_combine_kernel<64><<<ca.B * ca.H, 64 * kSpCombineWaves, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
                                                                              scores, ld, o, o32);
     }
