@@ -98,6 +98,11 @@ typedef struct qkv_cache {
     qkv_plane plane[QKV_MAX_LOOPS];
     uint16_t* tail_k[QKV_MAX_LOOPS];
     uint16_t* tail_v[QKV_MAX_LOOPS];
+    /* NULL, or device uint32 [batch][cap_ctx], zeroed before the first encode: bit p of a
+     * position's word is set iff the sparse plane of loop p+1 stores the position
+     * (kv_encode_loop maintains it).  With it, a gather over a deep chain reads only the
+     * planes that store a column; without it, it looks the column up in every plane. */
+    uint32_t* stored_loops;
 } qkv_cache;
 
 /* Human-readable text of a status code (static storage). */

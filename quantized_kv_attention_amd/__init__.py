@@ -38,7 +38,7 @@ class QkvCache(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("n_loops", ctypes.c_int32), ("cap_ctx", ctypes.c_int32), ("n_ctx", ctypes.c_int32),
                 ("plane", QkvPlane * MAX_LOOPS), ("tail_k", ctypes.c_void_p * MAX_LOOPS),
-                ("tail_v", ctypes.c_void_p * MAX_LOOPS)]
+                ("tail_v", ctypes.c_void_p * MAX_LOOPS), ("stored_loops", ctypes.c_void_p)]
 
 
 _lib = None

@@ -70,6 +70,10 @@ class LayerCache:
             self.tail_v.append(tv)
             desc.tail_k[r] = tk.data_ptr()
             desc.tail_v[r] = tv.data_ptr()
+        # which loops' sparse planes store each position (kept by the encoder; lets a gather
+        # over a deep chain skip the planes that do not store a column)
+        self.stored_loops = torch.zeros((batch, cap_ctx), dtype=torch.int32, device=device)
+        desc.stored_loops = self.stored_loops.data_ptr()
         self.desc = desc
         # host copy of each loop's activity for positions still in the tail
         self.act = np.zeros((n_loops, batch, cap_ctx), bool)

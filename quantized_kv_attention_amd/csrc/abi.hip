@@ -24,6 +24,8 @@ int make_arg(const qkv_cache* c, CacheArg* a) {
     a->n_ctx = c->n_ctx;
     a->n_body = body_len(c->n_ctx);
     a->nplanes = c->n_loops;
+    if (c->stored_loops && !aligned16(c->stored_loops)) return QKV_EINVAL;
+    a->smask = c->stored_loops;
     for (int p = 0; p < QKV_MAX_LOOPS; ++p) {
         PlaneArg& P = a->p[p];
         P = PlaneArg{};

@@ -43,6 +43,7 @@ struct CacheArg {
     PlaneArg p[QKV_MAX_LOOPS];
     const uint16_t* tail_k[QKV_MAX_LOOPS];
     const uint16_t* tail_v[QKV_MAX_LOOPS];
+    uint32_t* smask;   // [B][cap_ctx]: bit p set iff sparse plane p stores the position, or null
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t u16) { return __uint_as_float(u16 << 16); }
@@ -89,6 +90,17 @@ __device__ __forceinline__ float2 pair_xor32(float v) {
     return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float add_xor16(float v) { const float2 p = pair_xor16(v); return p.x + p.y; }
+// Bitwise OR over the wave (the raw bits move through the same lane exchanges).
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+    v |= __float_as_uint(dpp<0xB1>(__uint_as_float(v)));   // quad_perm [1,0,3,2]
+    v |= __float_as_uint(dpp<0x4E>(__uint_as_float(v)));   // quad_perm [2,3,0,1]
+    v |= __float_as_uint(dpp<0x141>(__uint_as_float(v)));  // row_half_mirror
+    v |= __float_as_uint(dpp<0x140>(__uint_as_float(v)));  // row_mirror
+    float2 p = pair_xor16(__uint_as_float(v));
+    v = __float_as_uint(p.x) | __float_as_uint(p.y);
+    p = pair_xor32(__uint_as_float(v));
+    return __float_as_uint(p.x) | __float_as_uint(p.y);
+}
 __device__ __forceinline__ float add_xor32(float v) { const float2 p = pair_xor32(v); return p.x + p.y; }
 
 // Whole-wave reductions, the result in every lane: DPP within each 16-lane row, then the

@@ -314,7 +314,8 @@ __global__ __launch_bounds__(256) void encode_maps_kernel(int cap_ctx, int pos0,
                                                           const int32_t* __restrict__ act_pos,
                                                           const int32_t* __restrict__ n_act, int ld_act,
                                                           int32_t* __restrict__ rowmap,
-                                                          int32_t* __restrict__ rowstart) {
+                                                          int32_t* __restrict__ rowstart,
+                                                          uint32_t* __restrict__ smask, uint32_t bit) {
     const int b = blockIdx.y;
     const int i = blockIdx.x * 256 + threadIdx.x;
     const int nstart = cap_ctx / 64 + 1;
@@ -328,7 +329,12 @@ __global__ __launch_bounds__(256) void encode_maps_kernel(int cap_ctx, int pos0,
             const int mid = (lo + hi) >> 1;
             if (a[mid] < p) lo = mid + 1; else hi = mid;
         }
-        rowmap[(size_t)b * cap_ctx + p] = (lo < na && a[lo] == p) ? base + lo : -1;
+        const bool stored = lo < na && a[lo] == p;
+        rowmap[(size_t)b * cap_ctx + p] = stored ? base + lo : -1;
+        if (smask) {
+            uint32_t& m = smask[(size_t)b * cap_ctx + p];
+            m = stored ? (m | bit) : (m & ~bit);
+        }
         if ((i & 63) == 0 && i > 0) rowstart[(size_t)b * nstart + p / 64] = base + lo;
     }
     if (i == 0) rowstart[(size_t)b * nstart + (pos0 + n_pos) / 64] = base + ((na + 63) / 64) * 64;
@@ -388,7 +394,8 @@ int launch_encode(const CacheArg& ca, int D, int loop, int pos0, int n_pos, cons
     if (!P.dense) {
         dim3 g2((n_pos + 255) / 256, ca.B);
         encode_maps_kernel<<<g2, 256, 0, st>>>(ca.cap_ctx, pos0, n_pos, act_pos, n_act, ld_act,
-                                               const_cast<int32_t*>(P.rowmap), const_cast<int32_t*>(P.rowstart));
+                                               const_cast<int32_t*>(P.rowmap), const_cast<int32_t*>(P.rowstart),
+                                               ca.smask, 1u << (loop - 1));
         if (hipGetLastError() != hipSuccess) return QKV_ELAUNCH;
     }
     return QKV_OK;

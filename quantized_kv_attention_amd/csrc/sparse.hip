@@ -97,6 +97,13 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 5) void sparse_chunk_ke
     const int32_t* id = idx + (size_t)bh * k;
     const float* ps = p_sel + (size_t)bh * k;
 
+    // planes of the chain (bit p: plane p), and those of them that are dense
+    const uint32_t chain_bits = loop >= 32 ? ~0u : ((1u << loop) - 1u);
+    uint32_t dense_bits = 0;
+    if constexpr (SB > 1) {
+        for (int p = 0; p < loop; ++p)
+            if (ca.p[p].dense) dense_bits |= 1u << p;
+    }
     // Deep chains: the chunk's entries whose column the first sparse plane stores (the long
     // chains) are taken first, spread over the first round of every wave, so that a wave
     // runs at most one long round while a chunk has no more long columns than a round has
@@ -117,7 +124,9 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 5) void sparse_chunk_ke
                 bool lng = false;
                 if (e < kChunk && i < k && probe >= 0) {
                     const int j = id[i];
-                    if (j >= 0 && j < ca.n_body) lng = ca.p[probe].rowmap[(size_t)b * cap + j] >= 0;
+                    if (j >= 0 && j < ca.n_body)
+                        lng = ca.smask ? (ca.smask[(size_t)b * cap + j] & chain_bits & ~dense_bits) != 0u
+                                       : ca.p[probe].rowmap[(size_t)b * cap + j] >= 0;
                 }
                 lm[t] = __ballot(lng);
                 vm[t] = __ballot(e < kChunk);
@@ -145,6 +154,18 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 5) void sparse_chunk_ke
         const bool valid = i < k && j >= 0 && j < ca.n_ctx;
         j = valid ? j : 0;
         const float pj = valid ? ps[i] : 0.f;
+        // deep chains: the planes some column of this wave needs (dense ones, and the sparse
+        // ones that store a column), visited in ascending order
+        uint32_t cm = 0u, todo = 0u;
+        if constexpr (SB > 1) {
+            if (ca.smask) {
+                cm = j < ca.n_body ? ca.smask[(size_t)b * cap + j] : 0u;
+                todo = (dense_bits | __builtin_amdgcn_readfirstlane(wave_or(cm))) & chain_bits;
+            } else {
+                cm = ~0u;
+                todo = chain_bits;
+            }
+        }
         float kh[8], vh[8], vc[8];
         if (j >= ca.n_body) {
             const size_t off = ((size_t)bh * kTail + (j % kTail)) * D + c0;
@@ -153,28 +174,36 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 5) void sparse_chunk_ke
             bf16x8(*reinterpret_cast<const uint4*>(ca.tail_v[loop - 2] + off), vh);
         } else {
             bool act_r = false;
-            // the column's slots are looked up SB planes at a time, all in flight together
-            // (they are independent), before any of those planes' data is read
-            for (int p0 = 0; p0 < loop; p0 += SB) {
-                int sl[SB];
+            if constexpr (SB > 1) {
+                // SB planes of the chain at a time: their slot lookups all in flight together,
+                // then all their data (a plane that does not store the column loads its
+                // block 0, weighted 0)
+                while (todo) {
+                    int pp[SB], sl[SB];
 #pragma unroll
-                for (int u = 0; u < SB; ++u) {
-                    sl[u] = -1;
-                    if (p0 + u < loop) {
-                        const PlaneArg& P = ca.p[p0 + u];
-                        sl[u] = P.dense ? j : P.rowmap[(size_t)b * cap + j];
+                    for (int u = 0; u < SB; ++u) {
+                        pp[u] = todo ? __builtin_ctz(todo) : -1;
+                        todo &= todo - 1u;
                     }
-                }
-                if constexpr (SB > 1) {
+#pragma unroll
+                    for (int u = 0; u < SB; ++u) {
+                        sl[u] = -1;
+                        if (pp[u] >= 0) {
+                            const PlaneArg& P = ca.p[pp[u]];
+                            if (P.dense)
+                                sl[u] = j;
+                            else if ((cm >> pp[u]) & 1u)
+                                sl[u] = P.rowmap[(size_t)b * cap + j];
+                        }
+                    }
                     uint32_t kw[SB], vw[SB];
                     float4 s0[SB], s1[SB], z0[SB], z1[SB];
                     float2 vm[SB];
                     bool act[SB];
 #pragma unroll
                     for (int u = 0; u < SB; ++u) {
-                        const int p = min(p0 + u, loop - 1);
-                        const PlaneArg& P = ca.p[p];
-                        act[u] = p0 + u < loop && sl[u] >= 0 && sl[u] < P.n_blocks * 64;
+                        const PlaneArg& P = ca.p[pp[u] >= 0 ? pp[u] : pp[0]];
+                        act[u] = pp[u] >= 0 && sl[u] >= 0 && sl[u] < P.n_blocks * 64;
                         const int slot = act[u] ? sl[u] : 0;
                         const uint8_t* bp = block_ptr<D>(P, ca.H, b, h, slot >> 6);
                         const int row = slot & 63;
@@ -189,7 +218,7 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 5) void sparse_chunk_ke
                     }
 #pragma unroll
                     for (int u = 0; u < SB; ++u) {
-                        const int p = p0 + u;
+                        const int p = pp[u];
                         if (!act[u]) continue;
                         const float ks[8] = {s0[u].x, s0[u].y, s0[u].z, s0[u].w, s1[u].x, s1[u].y, s1[u].z, s1[u].w};
                         const float kz[8] = {z0[u].x, z0[u].y, z0[u].z, z0[u].w, z1[u].x, z1[u].y, z1[u].z, z1[u].w};
@@ -213,7 +242,19 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 5) void sparse_chunk_ke
                             for (int c = 0; c < 8; ++c) vc[c] = vh[c] + fmaf(code[c], vm[u].x, vm[u].y);
                         }
                     }
-                } else {
+                }
+            } else {
+                // one plane at a time: its slot, then its data
+                for (int p0 = 0; p0 < loop; p0 += SB) {
+                    int sl[SB];
+#pragma unroll
+                    for (int u = 0; u < SB; ++u) {
+                        sl[u] = -1;
+                        if (p0 + u < loop) {
+                            const PlaneArg& P = ca.p[p0 + u];
+                            sl[u] = P.dense ? j : P.rowmap[(size_t)b * cap + j];
+                        }
+                    }
 #pragma unroll
                     for (int u = 0; u < SB; ++u) {
                         const int p = p0 + u;

@@ -87,6 +87,40 @@ def test_deep_recurrence_32_loops():
     check_step(p, p.queries(0), w.n_dense, w.k_cols(900), "R=32")
 
 
+def test_deep_chain_stored_loops_mask():
+    # the per-position mask of the loops whose sparse planes store a position matches the
+    # planes' contents, and the deep-chain gather gives the same bits with and without it
+    w = dataclasses.replace(W["deep32"], H=2)
+    p = Pair(w, n=900, extra=70)
+    c = p.gpu
+    mask = c.stored_loops.cpu().numpy().view(np.uint32)
+    for b in range(w.B):
+        for r in range(w.R):
+            if c.dense[r]:
+                continue
+            pos = p.orc.planes[b][0][r].pos
+            stored = np.zeros(c.cap, bool)
+            stored[pos[pos >= 0]] = True
+            assert np.array_equal((mask[b] >> r) & 1 == 1, stored), f"loop {r + 1} mask"
+    q = [to_dev_bf16(x) for x in p.queries(0)]
+    k = w.k_cols(900)
+
+    def run():
+        qcache.decode_step(c, p.bufs, q, w.n_dense, k)
+        torch.cuda.synchronize()
+        return p.bufs.o_f32.clone(), p.bufs.scores[:, :, :c.n_ctx].clone(), p.bufs.lse.clone()
+
+    with_mask = run()
+    keep = c.desc.stored_loops
+    c.desc.stored_loops = None
+    try:
+        without = run()
+    finally:
+        c.desc.stored_loops = keep
+    for a_, b_ in zip(with_mask, without):
+        assert torch.equal(a_, b_)
+
+
 def test_all_columns_is_dense_on_gpu():
     w = dataclasses.replace(W["ctx4k"], H=2)
     p = Pair(w, n=777, extra=8)
