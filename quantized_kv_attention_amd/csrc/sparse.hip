@@ -51,13 +51,15 @@ __device__ __forceinline__ void store_new_row(NewRow nr, uint16_t* tk, uint16_t*
 }
 
 // SB: planes whose slots and data a column loads together.  SB = 1 (chains of up to four
-// planes) keeps the kernel at 92 VGPRs, 5 waves per SIMD.  SB = 3 (deeper chains, whose
+// planes) compiles to 92 VGPRs, 5 waves per SIMD, with no occupancy hint: a hint of 5 waves
+// makes the scheduler trade 64-bit moves for selects and costs about 1.5 us per call at
+// 32K context.  SB = 3 (deeper chains, whose
 // loads would otherwise be one memory latency per plane) issues a batch's slot lookups
 // together and then every plane's data of the batch together; a plane that does not store
 // the column loads its block 0 and weighs it 0, so every plane must hold a block.  It
 // runs at 3 waves per SIMD (up to 168 VGPRs).
 template <int D, int SB>
-__global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 5) void sparse_chunk_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 1) void sparse_chunk_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                            NewRow nr, float sm, const int32_t* __restrict__ idx,
                                                            const float* __restrict__ p_sel, int k,
                                                            float* __restrict__ cs,
