@@ -202,6 +202,18 @@ def main():
     print(f"[bench] {K} steps x {L} layers: {total_ms:.2f} ms (wall {wall * 1e3:.2f} ms), "
           f"{us_step_layer:.2f} us per layer-step", file=sys.stderr, flush=True)
 
+    # the same step launched eagerly (no graph), flush excluded
+    Ke = min(K, 16)
+    e0.record()
+    for _ in range(Ke):
+        step(False)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1000.0 / (Ke * L)
+    print(f"[bench] eager (no graph), {Ke} steps without flush: {eager_us:.2f} us per layer-step",
+          file=sys.stderr, flush=True)
+    ceiling = read_ceiling()
+
     # ---- algorithmic bytes of one layer-step (from the actual masks and selections) ----
     c0, b0, act0 = layers[0]["c"], layers[0]["b"], layers[0]["act"]
     T = n_step - nb
@@ -278,10 +290,13 @@ def main():
           f"-> {achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
     traffic = read_traffic()
+    full_chain_bytes = sum(w.H * bm.dense_loop_bytes([rows[p][b] for p in range(w.R)], T, n_step, d)
+                           for b in range(B))
 
     rows_out = None
     if not args.no_rows:
-        rows_out = measure_rows(w, layers, stack, dense, n, nb, k, loop_bytes, flush_loop_bytes, append_bytes, args)
+        rows_out = measure_rows(w, layers, stack, dense, n, nb, k, loop_bytes, flush_loop_bytes, append_bytes,
+                                full_chain_bytes, args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -307,6 +322,8 @@ def main():
                    "selection": ("one call per layer" if args.select_per_layer
                                  else f"one call per sparse loop for all {L} layers"),
                    "value_is": "microseconds per decode step of one layer"},
+        "eager_us_per_layer_step": round(eager_us, 3),
+        "read_ceiling": ceiling,
         "hbm_GBps_step": round(gbps_step, 1),
         "pct_peak_step": round(100 * gbps_step / HBM_PEAK_GBPS, 2),
         "bytes_per_layer_step": int(step_bytes),
@@ -322,6 +339,32 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def read_ceiling():
+    """A read-only reference on the same device: the library's plain streaming read of 2 GiB
+    (nothing but loads), next to the 8 TB/s peak."""
+    import torch
+    import quantized_kv_attention_amd as qkv
+    x = torch.zeros(1 << 31, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(qkv.STREAM_READ_GROUPS, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    qkv.stream_read(x, sink, s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record(s)
+    for _ in range(reps):
+        qkv.stream_read(x, sink, s)
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    gbps = x.numel() / (us * 1e-6) / 1e9
+    del x, sink
+    torch.cuda.empty_cache()
+    print(f"[bench] read ceiling (plain streaming read of 2 GiB): {gbps:.0f} GB/s", file=sys.stderr, flush=True)
+    return {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "how": "qkv_stream_read over 2 GiB, HIP events around 10 calls"}
+
+
 def _dense_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -330,7 +373,8 @@ def _dense_source_hash():
     return h.hexdigest()[:16]
 
 
-def measure_rows(w, layers, stack, dense, n, nb, k, loop_bytes, flush_loop_bytes, append_bytes, args):
+def measure_rows(w, layers, stack, dense, n, nb, k, loop_bytes, flush_loop_bytes, append_bytes, full_chain_bytes,
+                 args):
     """Each entry point of the path timed on its own (events around back-to-back calls over
     the rotated layers), with its algorithmic bytes and the fraction of the HBM peak."""
     import numpy as np
@@ -387,6 +431,13 @@ def measure_rows(w, layers, stack, dense, n, nb, k, loop_bytes, flush_loop_bytes
             t = timed(lambda: [sp(ly) for ly in layers])
             sel_b = w.B * w.H * bm.select_bytes(n + 1, k)
             out[f"attn_decode_sparse loop {loop}"] = row(t, L, loop_bytes[loop - 1] - sel_b)
+
+    # the last loop read densely through its whole chain (every plane, sparse ones by their
+    # row maps), for comparison with the sparse splice; overwrites that loop's outputs only
+    R = w.R
+    t = timed(lambda: [qkv.attn_decode_dense(ly["c"], R, ly["q"][R - 1], 1.0, ly["b"].o[R - 1], ly["b"].o_f32[R - 1],
+                                             ly["b"].scores, ly["b"].lse, ly["b"].ws, s) for ly in layers])
+    out[f"attn_decode_dense loop {R} (full chain, {R} planes)"] = row(t, L, full_chain_bytes)
 
     # token append into every loop's tail, and the 64-row flush of every loop
     t = timed(lambda: [qkv.kv_append_tail(ly["c"], 0, n, ly["kn"], ly["vn"], s) for ly in layers])

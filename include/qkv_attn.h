@@ -206,6 +206,20 @@ int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, cons
                        const float* o_prev, const float* lse, float* scores, int ld_scores,
                        uint16_t* o, float* o_f32, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * qkv_stream_read - bandwidth reference, not part of the attention path: reads n_bytes from
+ * src with a plain streaming kernel (QKV_STREAM_READ_GROUPS workgroups of 256 lanes, 8
+ * 16-byte loads per lane in flight), so that the readers' rates can be set beside what a
+ * read with nothing else to do reaches on the same device.
+ *   src   device memory, 16-byte aligned; n_bytes > 0, a multiple of 16.
+ *   sink  device uint32 [QKV_STREAM_READ_GROUPS], 16-byte aligned, caller-owned: workgroup g
+ *         stores the XOR of every 32-bit word it read, where it reads the 16-byte words
+ *         w with (w / 2048) % QKV_STREAM_READ_GROUPS == g.
+ * Asynchronous on `stream`.  QKV_EINVAL on a bad argument (nothing launched).
+ */
+#define QKV_STREAM_READ_GROUPS 2048
+int qkv_stream_read(const void* src, size_t n_bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,8 @@ TAIL_SLOTS = 128
 QKV_OK, QKV_EINVAL, QKV_EUNSUPPORTED, QKV_ECAPACITY, QKV_ELAUNCH, QKV_EWORKSPACE = 0, -1, -2, -3, -4, -5
 
 EXPORTED = ("qkv_strerror", "qkv_block_bytes", "qkv_body_len", "qkv_workspace_bytes", "kv_encode_loop",
-            "kv_append_tail", "attn_decode_dense", "select_columns", "attn_decode_sparse")
+            "kv_append_tail", "attn_decode_dense", "select_columns", "attn_decode_sparse", "qkv_stream_read")
+STREAM_READ_GROUPS = 2048
 
 
 class QkvError(RuntimeError):
@@ -70,6 +71,8 @@ def lib():
     L.attn_decode_dense.restype = i32
     L.select_columns.argtypes = [vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.select_columns.restype = i32
+    L.qkv_stream_read.argtypes = [vp, sz, vp, vp]
+    L.qkv_stream_read.restype = i32
     L.attn_decode_sparse.argtypes = [cp, i32, vp, vp, vp, f32, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     L.attn_decode_sparse.restype = i32
     _lib = L
@@ -159,3 +162,12 @@ def attn_decode_sparse(cache, loop, q, sm_scale, idx, p_sel, mass, k, o_prev, ls
 
 
 from .cache import LayerCache, DecodeBuffers  # noqa: E402
+
+
+def stream_read(src, sink, stream=None):
+    """Bandwidth reference (not part of the attention path): reads every byte of the device
+    tensor `src` with a plain streaming kernel; `sink` is a device int32 tensor of
+    STREAM_READ_GROUPS words (each workgroup's XOR of the 32-bit words it read)."""
+    assert src.is_cuda and sink.is_cuda and sink.numel() >= STREAM_READ_GROUPS and sink.element_size() == 4
+    _check("qkv_stream_read", lib().qkv_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                                   _stream(stream)))

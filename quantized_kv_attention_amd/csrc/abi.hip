@@ -187,4 +187,10 @@ int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, cons
                          lse, scores, ld_scores, o, o_f32, ws, to_stream(stream));
 }
 
+int qkv_stream_read(const void* src, size_t n_bytes, uint32_t* sink, void* stream) {
+    if (!src || !sink || n_bytes == 0 || (n_bytes % 16) != 0 || !aligned16(src) || !aligned16(sink))
+        return QKV_EINVAL;
+    return launch_stream_read(src, n_bytes, sink, to_stream(stream));
+}
+
 }  // extern "C"

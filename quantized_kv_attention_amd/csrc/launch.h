@@ -33,6 +33,7 @@ size_t select_ws_bytes(int B, int H, int n);
 int launch_select(const float* scores, int ld, const float* lse, int B, int H, int n, int k, int32_t* idx,
                   float* p_sel, float* mass, void* ws, hipStream_t st);
 
+int launch_stream_read(const void* src, size_t n_bytes, uint32_t* sink, hipStream_t st);
 size_t sparse_ws_bytes(int B, int H, int D, int k);
 int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, const int32_t* idx,
                   const float* p_sel, const float* mass, int k, const float* o_prev, const float* lse,

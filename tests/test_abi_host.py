@@ -98,6 +98,12 @@ def test_argument_validation():
     # select: k above n
     assert L.select_columns(vp(16), 256, vp(16), 1, 1, 256, 257, vp(16), vp(16), vp(16), None, 0, None) == qkv.QKV_EINVAL
     assert L.kv_append_tail(ctypes.byref(d), 1, 0, 129, vp(16), vp(16), None) == qkv.QKV_EINVAL
+    # stream read: null source, empty, ragged length, misaligned source or sink
+    assert L.qkv_stream_read(None, 64, vp(16), None) == qkv.QKV_EINVAL
+    assert L.qkv_stream_read(vp(16), 0, vp(16), None) == qkv.QKV_EINVAL
+    assert L.qkv_stream_read(vp(16), 40, vp(16), None) == qkv.QKV_EINVAL
+    assert L.qkv_stream_read(vp(24), 64, vp(16), None) == qkv.QKV_EINVAL
+    assert L.qkv_stream_read(vp(16), 64, vp(20), None) == qkv.QKV_EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
