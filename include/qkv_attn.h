@@ -56,8 +56,12 @@ enum {
 /*
  * One loop's stored plane (loop p = index + 1).  Layout of `data`, device memory:
  *   [batch][heads][n_blocks][block], one block = 64 consecutive storage slots, with
- *   block = K codes [64][d/2] | V codes [64][d/2] | K s[d], K z[d] (fp32)
- *           | V meta [64][d/64] of (s, z) (fp32)                   -> qkv_block_bytes(d)
+ *   d = 128: block = K codes [64][64] | V records [64] of (V codes [64] | (s, z) [2], fp32)
+ *                    | K s[128], K z[128] (fp32)                    -> 10240 bytes
+ *   d = 64:  block = K codes [64][32] | V codes [64][32] | K s[64], K z[64] (fp32)
+ *                    | V meta [64] of (s, z) (fp32)                 -> 5120 bytes
+ *   (at d = 128 a slot's value codes and value meta are adjacent, 80 bytes per slot, so a
+ *   gather of one slot's value touches fewer 128-byte lines).
  *   A code byte holds channel 2i in its low nibble and channel 2i+1 in its high nibble.
  *   Key group = one block (64 consecutive slots) per channel; value group = one slot
  *   over 64 consecutive channels.  Dequantised value = fmaf(code, s, z).

@@ -16,12 +16,24 @@ constexpr int kWave = 64;
 template <int D>
 struct Block {
     static constexpr int kRowBytes = D / 2;             // packed codes of one slot
-    static constexpr int kKc = 0;                       // K codes [64][D/2]
-    static constexpr int kVc = 64 * D / 2;              // V codes [64][D/2]
-    static constexpr int kKm = 64 * D;                  // K s[D], z[D]
-    static constexpr int kVm = 64 * D + D * 8;          // V [64][D/64] x (s, z)
-    static constexpr int kBytes = kVm + 64 * (D / 64) * 8;
     static constexpr int kVGroups = D / 64;
+    // d = 128: K codes [64][64] | V records [64][64 code bytes + 2 x (s, z)] | K s[D], z[D].
+    // A slot's value codes and value meta sit together (80 bytes), so a gathered slot's
+    // value takes 1.5 lines of 128 bytes on average instead of 2.
+    // d = 64: K codes [64][32] | V codes [64][32] | K s[D], z[D] | V meta [64] x (s, z)
+    // (a 40-byte record would break the 16-byte alignment of the code loads).
+    static constexpr bool kVRec = (D == 128);
+    static constexpr int kKc = 0;                                            // K codes [64][D/2]
+    static constexpr int kV = 64 * D / 2;                                    // value region
+    static constexpr int kVStride = kVRec ? D / 2 + kVGroups * 8 : D / 2;    // value codes: bytes per slot
+    static constexpr int kKm = kVRec ? kV + 64 * kVStride : 64 * D;         // K s[D], z[D]
+    static constexpr int kVmArr = 64 * D + D * 8;                            // d = 64: V meta array
+    static constexpr int kBytes = kVRec ? kKm + D * 8 : kVmArr + 64 * kVGroups * 8;
+    // offsets of slot `row`'s value codes and of its value meta (s, z) for group 0
+    __host__ __device__ static constexpr int vc(int row) { return kV + row * kVStride; }
+    __host__ __device__ static constexpr int vm(int row) {
+        return kVRec ? kV + row * kVStride + D / 2 : kVmArr + row * kVGroups * 8;
+    }
     // lanes per row when each lane owns 32 channels (16 code bytes)
     static constexpr int kLpr = D / 32;
     static constexpr int kRpi = kWave / kLpr;           // rows covered by one wave load

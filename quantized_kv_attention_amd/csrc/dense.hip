@@ -84,8 +84,8 @@ __device__ __forceinline__ void vpass_block(const uint8_t* bp, int prt, int rsub
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
         const int row = rsub + RPI * it;
-        w[it] = *reinterpret_cast<const uint4*>(bp + Block<D>::kVc + row * (D / 2) + prt * 16);
-        m[it] = *reinterpret_cast<const float2*>(bp + Block<D>::kVm + (row * (D / 64) + (prt >> 1)) * 8);
+        w[it] = *reinterpret_cast<const uint4*>(bp + Block<D>::vc(row) + prt * 16);
+        m[it] = *reinterpret_cast<const float2*>(bp + Block<D>::vm(row) + (prt >> 1) * 8);
     }
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
@@ -305,8 +305,8 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
 #pragma unroll
                 for (int it = 0; it < NLD; ++it) {
                     const int row = rsub + RPI * it;
-                    wv[p][it] = *reinterpret_cast<const uint4*>(bp + Block<D>::kVc + row * (D / 2) + prt * 16);
-                    mv[p][it] = *reinterpret_cast<const float2*>(bp + Block<D>::kVm + (row * (D / 64) + (prt >> 1)) * 8);
+                    wv[p][it] = *reinterpret_cast<const uint4*>(bp + Block<D>::vc(row) + prt * 16);
+                    mv[p][it] = *reinterpret_cast<const float2*>(bp + Block<D>::vm(row) + (prt >> 1) * 8);
                 }
             }
         };

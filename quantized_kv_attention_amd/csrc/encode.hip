@@ -148,8 +148,8 @@ __global__ __launch_bounds__(256) void encode_group_kernel(CacheArg ca, int loop
                     if (slot >= 0) {
                         const uint8_t* bq = block_ptr<D>(Q, ca.H, b, h, slot >> 6);
                         const int rw = slot & 63;
-                        cw[it] = *reinterpret_cast<const uint32_t*>(bq + (kind ? Block<D>::kVc : Block<D>::kKc) +
-                                                                   rw * (D / 2) + c0 / 2);
+                        cw[it] = *reinterpret_cast<const uint32_t*>(
+                            bq + (kind ? Block<D>::vc(rw) : Block<D>::kKc + rw * (D / 2)) + c0 / 2);
                         if (kind == 0) {
                             const float* m = reinterpret_cast<const float*>(bq + Block<D>::kKm) + c0;
                             const float4 sa = *reinterpret_cast<const float4*>(m);
@@ -161,8 +161,7 @@ __global__ __launch_bounds__(256) void encode_group_kernel(CacheArg ca, int loop
                             z8[it][0] = za.x; z8[it][1] = za.y; z8[it][2] = za.z; z8[it][3] = za.w;
                             z8[it][4] = zb.x; z8[it][5] = zb.y; z8[it][6] = zb.z; z8[it][7] = zb.w;
                         } else {
-                            const float2 vm = *reinterpret_cast<const float2*>(bq + Block<D>::kVm +
-                                                                               (rw * (D / 64) + (c0 >> 6)) * 8);
+                            const float2 vm = *reinterpret_cast<const float2*>(bq + Block<D>::vm(rw) + (c0 >> 6) * 8);
 #pragma unroll
                             for (int c = 0; c < CH; ++c) {
                                 s8[it][c] = vm.x;
@@ -290,7 +289,7 @@ __global__ __launch_bounds__(256) void encode_group_kernel(CacheArg ca, int loop
         const int kind = e / (64 * NCP / 16), rest = e % (64 * NCP / 16);
         const int row = rest / (NCP / 16), byte0 = (rest % (NCP / 16)) * 16;
         const uint4 w = *reinterpret_cast<const uint4*>(&pk[kind][row][byte0]);
-        *reinterpret_cast<uint4*>(blk + (kind ? Block<D>::kVc : Block<D>::kKc) + row * (D / 2) + byte0) = w;
+        *reinterpret_cast<uint4*>(blk + (kind ? Block<D>::vc(row) : Block<D>::kKc + row * (D / 2)) + byte0) = w;
     }
     {
         float* m = reinterpret_cast<float*>(blk + Block<D>::kKm);
@@ -298,10 +297,10 @@ __global__ __launch_bounds__(256) void encode_group_kernel(CacheArg ca, int loop
             m[c] = ks[c];
             m[D + c] = kz[c];
         }
-        float* mv = reinterpret_cast<float*>(blk + Block<D>::kVm);
         for (int e = tid; e < 64 * VG; e += 256) {
-            mv[2 * e] = vs[e / VG][e % VG];
-            mv[2 * e + 1] = vz[e / VG][e % VG];
+            float* mv = reinterpret_cast<float*>(blk + Block<D>::vm(e / VG)) + 2 * (e % VG);
+            mv[0] = vs[e / VG][e % VG];
+            mv[1] = vz[e / VG][e % VG];
         }
     }
 

@@ -44,10 +44,18 @@ def unpack_plane(cache: qcache.LayerCache, r: int, b: int, h: int, nslots: int):
         out[:, 0::2] = x & 15
         out[:, 1::2] = x >> 4
         return out
+    g = d // 64
     kc = nib(raw[:, 0:32 * d])
-    vc = nib(raw[:, 32 * d:64 * d])
-    km = np.ascontiguousarray(raw[:, 64 * d:72 * d]).view(np.float32).reshape(nb, 2, d)
-    vm = np.ascontiguousarray(raw[:, 72 * d:72 * d + 64 * (d // 64) * 8]).view(np.float32).reshape(nb * 64, d // 64, 2)
+    if d == 128:  # value records: 64 code bytes + (s, z) per group, per slot; then key meta
+        rec = raw[:, 32 * d:32 * d + 64 * (d // 2 + 8 * g)].reshape(nb, 64, d // 2 + 8 * g)
+        vc = nib(np.ascontiguousarray(rec[:, :, :d // 2]))
+        vm = np.ascontiguousarray(rec[:, :, d // 2:]).view(np.float32).reshape(nb * 64, g, 2)
+        km0 = 32 * d + 64 * (d // 2 + 8 * g)
+    else:
+        vc = nib(raw[:, 32 * d:64 * d])
+        vm = np.ascontiguousarray(raw[:, 72 * d:72 * d + 64 * g * 8]).view(np.float32).reshape(nb * 64, g, 2)
+        km0 = 64 * d
+    km = np.ascontiguousarray(raw[:, km0:km0 + 8 * d]).view(np.float32).reshape(nb, 2, d)
     return dict(kc=kc[:nslots], vc=vc[:nslots], ks=km[:, 0], kz=km[:, 1], vs=vm[:nslots, :, 0], vz=vm[:nslots, :, 1])
 
 
