@@ -36,12 +36,14 @@ __device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float 
 // One workgroup encodes one group of up to 64 stored rows of one (sequence, head).  Thread
 // items are 8 channels of one row (one 16-byte load of bf16); for loop r >= 2 each item
 // rebuilds the 8 channels of Xhat^(r-1) through planes 1..r-1 (one code word and its scales
-// per plane; the rows' slots are looked up once per group) and subtracts it.  Keys are
-// quantised per channel over the rows (a thread per channel pair and 16 rows), values per
-// row over each 64-channel group (8 lanes of 8 channels each); codes are packed into bytes
-// in LDS as they are made and the block is written with 16-byte stores.
+// per plane; the rows' slots are looked up once per group) and subtracts it.  The residuals
+// stay in registers: keys are quantised per channel over the rows (each thread's rows, then
+// shuffles between the lanes that hold the same channels, then the four waves through LDS),
+// values per row over each 64-channel group (shuffles among the group's 8 lanes), and each
+// thread stores its own code words and metadata into the block.  Three workgroups per CU
+// (at most 168 VGPRs).
 template <int D>
-__global__ __launch_bounds__(256) void encode_group_kernel(CacheArg ca, int loop, int pos0, int n_pos,
+__global__ __launch_bounds__(256, 3) void encode_group_kernel(CacheArg ca, int loop, int pos0, int n_pos,
                                                            const int32_t* __restrict__ act_pos,
                                                            const int32_t* __restrict__ n_act, int ld_act,
                                                            const uint16_t* __restrict__ ksrc,
@@ -50,11 +52,7 @@ __global__ __launch_bounds__(256) void encode_group_kernel(CacheArg ca, int loop
     constexpr int CH = 8;                // channels per item
     constexpr int IPR = D / CH;          // items per row
     constexpr int NIT = 64 * IPR / 256;  // items per thread
-    constexpr int XS = D + 4;            // LDS row stride of X in floats (keeps 16-byte alignment)
-    constexpr int NCP = D / 2;           // channel pairs (code bytes per row)
-    constexpr int KPARTS = 256 / NCP;    // row parts of the key pass
-    constexpr int KROWS = 64 / KPARTS;
-    constexpr int VG = D / 64;           // value groups per row
+    constexpr int IB = NIT >= 2 ? 2 : 1;  // items whose chain loads go out together
     const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const PlaneArg& P = ca.p[loop - 1];
@@ -72,19 +70,9 @@ __global__ __launch_bounds__(256) void encode_group_kernel(CacheArg ca, int loop
     const int nch = loop - 1;           // planes of the chain Xhat^(r-1)
     const size_t bh = (size_t)b * ca.H + h;
 
-    __shared__ __align__(16) float Xk[64 * D];        // key residuals (read along rows)
-    __shared__ __align__(16) float Xv[64 * XS];       // value residuals (padded rows: read across rows)
-    // packed codes [kind][row][channel pair]; before any code is written the same bytes
-    // hold the per-part channel minima and maxima of the key pass
-    __shared__ __align__(16) uint8_t pkbuf[2 * 64 * NCP];
-    static_assert(2 * 64 * NCP >= 2 * KPARTS * D * (int)sizeof(float), "key-pass scratch");
-    uint8_t (*pk)[64][NCP] = reinterpret_cast<uint8_t (*)[64][NCP]>(pkbuf);
-    float (*red_mn)[D] = reinterpret_cast<float (*)[D]>(pkbuf);
-    float (*red_mx)[D] = reinterpret_cast<float (*)[D]>(pkbuf) + KPARTS;
     __shared__ int spos[64];
     extern __shared__ int sslot[];                  // [nch][64], sized at launch
-    __shared__ float ks[D], kz[D];
-    __shared__ float vs[64][VG], vz[64][VG];
+    __shared__ __align__(16) float red_mn[4][D], red_mx[4][D];  // per-wave key-channel minima, maxima
 
     if (tid < 64) {
         int p = -1;
@@ -105,21 +93,23 @@ __global__ __launch_bounds__(256) void encode_group_kernel(CacheArg ca, int loop
     }
     __syncthreads();
 
-    // ---- residuals of both kinds into LDS ----
+    // ---- per kind: this thread's items (8 channels of a row) in registers: residual,
+    //      quantisation and the block's bytes, stored directly ----
     int ipos[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int row = (tid + 256 * it) / IPR;
         ipos[it] = row < nr ? spos[row] : -1;
     }
+    const int lane = tid & 63, wave = tid >> 6;
+    const int c0 = (tid % IPR) * CH;  // every item of this thread covers these channels
     for (int kind = 0; kind < 2; ++kind) {
         const uint16_t* src = kind ? vsrc : ksrc;
         const uint16_t* tail = kind ? ca.tail_v[loop - 1] : ca.tail_k[loop - 1];
         float x[NIT][CH];
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int item = tid + 256 * it;
-            const int row = item / IPR, c0 = (item % IPR) * CH;
+            const int row = (tid + 256 * it) / IPR;
 #pragma unroll
             for (int c = 0; c < CH; ++c) x[it][c] = 0.f;
             if (ipos[it] >= 0) {
@@ -136,51 +126,54 @@ __global__ __launch_bounds__(256) void encode_group_kernel(CacheArg ca, int loop
                 for (int c = 0; c < CH; ++c) acc[it][c] = 0.f;
             for (int p = 0; p < nch; ++p) {
                 const PlaneArg& Q = ca.p[p];
-                // every item's code word and scales of this plane, then the dequantised sums
-                uint32_t cw[NIT];
-                float s8[NIT][CH], z8[NIT][CH];
+                // IB items at a time: their code words and scales of this plane in flight
+                // together, then the dequantised sums
 #pragma unroll
-                for (int it = 0; it < NIT; ++it) {
-                    const int item = tid + 256 * it;
-                    const int row = item / IPR, c0 = (item % IPR) * CH;
-                    const int slot = ipos[it] >= 0 ? sslot[p * 64 + row] : -1;
-                    cw[it] = 0;
-                    if (slot >= 0) {
-                        const uint8_t* bq = block_ptr<D>(Q, ca.H, b, h, slot >> 6);
-                        const int rw = slot & 63;
-                        cw[it] = *reinterpret_cast<const uint32_t*>(
-                            bq + (kind ? Block<D>::vc(rw) : Block<D>::kKc + rw * (D / 2)) + c0 / 2);
-                        if (kind == 0) {
-                            const float* m = reinterpret_cast<const float*>(bq + Block<D>::kKm) + c0;
-                            const float4 sa = *reinterpret_cast<const float4*>(m);
-                            const float4 sb = *reinterpret_cast<const float4*>(m + 4);
-                            const float4 za = *reinterpret_cast<const float4*>(m + D);
-                            const float4 zb = *reinterpret_cast<const float4*>(m + D + 4);
-                            s8[it][0] = sa.x; s8[it][1] = sa.y; s8[it][2] = sa.z; s8[it][3] = sa.w;
-                            s8[it][4] = sb.x; s8[it][5] = sb.y; s8[it][6] = sb.z; s8[it][7] = sb.w;
-                            z8[it][0] = za.x; z8[it][1] = za.y; z8[it][2] = za.z; z8[it][3] = za.w;
-                            z8[it][4] = zb.x; z8[it][5] = zb.y; z8[it][6] = zb.z; z8[it][7] = zb.w;
-                        } else {
-                            const float2 vm = *reinterpret_cast<const float2*>(bq + Block<D>::vm(rw) + (c0 >> 6) * 8);
+                for (int i0 = 0; i0 < NIT; i0 += IB) {
+                    uint32_t cw[IB];
+                    float s8[IB][CH], z8[IB][CH];
 #pragma unroll
-                            for (int c = 0; c < CH; ++c) {
-                                s8[it][c] = vm.x;
-                                z8[it][c] = vm.y;
+                    for (int u = 0; u < IB; ++u) {
+                        const int row = (tid + 256 * (i0 + u)) / IPR;
+                        const int slot = ipos[i0 + u] >= 0 ? sslot[p * 64 + row] : -1;
+                        cw[u] = 0;
+                        if (slot >= 0) {
+                            const uint8_t* bq = block_ptr<D>(Q, ca.H, b, h, slot >> 6);
+                            const int rw = slot & 63;
+                            cw[u] = *reinterpret_cast<const uint32_t*>(
+                                bq + (kind ? Block<D>::vc(rw) : Block<D>::kKc + rw * (D / 2)) + c0 / 2);
+                            if (kind == 0) {
+                                const float* m = reinterpret_cast<const float*>(bq + Block<D>::kKm) + c0;
+                                const float4 sa = *reinterpret_cast<const float4*>(m);
+                                const float4 sb = *reinterpret_cast<const float4*>(m + 4);
+                                const float4 za = *reinterpret_cast<const float4*>(m + D);
+                                const float4 zb = *reinterpret_cast<const float4*>(m + D + 4);
+                                s8[u][0] = sa.x; s8[u][1] = sa.y; s8[u][2] = sa.z; s8[u][3] = sa.w;
+                                s8[u][4] = sb.x; s8[u][5] = sb.y; s8[u][6] = sb.z; s8[u][7] = sb.w;
+                                z8[u][0] = za.x; z8[u][1] = za.y; z8[u][2] = za.z; z8[u][3] = za.w;
+                                z8[u][4] = zb.x; z8[u][5] = zb.y; z8[u][6] = zb.z; z8[u][7] = zb.w;
+                            } else {
+                                const float2 vm = *reinterpret_cast<const float2*>(bq + Block<D>::vm(rw) + (c0 >> 6) * 8);
+#pragma unroll
+                                for (int c = 0; c < CH; ++c) {
+                                    s8[u][c] = vm.x;
+                                    z8[u][c] = vm.y;
+                                }
                             }
                         }
                     }
-                }
 #pragma unroll
-                for (int it = 0; it < NIT; ++it) {
-                    const int item = tid + 256 * it;
-                    const int row = item / IPR;
-                    if (ipos[it] < 0 || sslot[p * 64 + row] < 0) continue;  // not stored in loop p+1: keeps loop p's value
+                    for (int u = 0; u < IB; ++u) {
+                        const int it = i0 + u;
+                        const int row = (tid + 256 * it) / IPR;
+                        if (ipos[it] < 0 || sslot[p * 64 + row] < 0) continue;  // not stored in loop p+1: keeps loop p's value
 #pragma unroll
-                    for (int c = 0; c < CH; ++c) {
-                        const uint32_t byte = (cw[it] >> (8 * (c >> 1))) & 0xFFu;
-                        const float code = (float)((c & 1) ? (byte >> 4) : (byte & 15u));
-                        const float deq = __builtin_fmaf(code, s8[it][c], z8[it][c]);
-                        acc[it][c] = (p == 0) ? deq : acc[it][c] + deq;
+                        for (int c = 0; c < CH; ++c) {
+                            const uint32_t byte = (cw[u] >> (8 * (c >> 1))) & 0xFFu;
+                            const float code = (float)((c & 1) ? (byte >> 4) : (byte & 15u));
+                            const float deq = __builtin_fmaf(code, s8[u][c], z8[u][c]);
+                            acc[it][c] = (p == 0) ? deq : acc[it][c] + deq;
+                        }
                     }
                 }
             }
@@ -190,117 +183,108 @@ __global__ __launch_bounds__(256) void encode_group_kernel(CacheArg ca, int loop
 #pragma unroll
                     for (int c = 0; c < CH; ++c) x[it][c] = x[it][c] - acc[it][c];
         }
-        float* Xd = kind ? Xv : Xk;
-        const int xs = kind ? XS : D;
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int item = tid + 256 * it;
-            const int row = item / IPR, c0 = (item % IPR) * CH;
-            *reinterpret_cast<float4*>(&Xd[row * xs + c0]) = make_float4(x[it][0], x[it][1], x[it][2], x[it][3]);
-            *reinterpret_cast<float4*>(&Xd[row * xs + c0 + 4]) = make_float4(x[it][4], x[it][5], x[it][6], x[it][7]);
-        }
-    }
-    __syncthreads();
 
-    // ---- keys: per channel over the group's stored rows; thread = channel pair x row part ----
-    {
-        const int cp = tid % NCP, part = tid / NCP;
-        const int ca0 = 2 * cp;
-        float mn0 = __builtin_huge_valf(), mx0 = -__builtin_huge_valf(), mn1 = mn0, mx1 = mx0;
-        for (int r = part * KROWS; r < (part + 1) * KROWS && r < nr; ++r) {
-            const float2 v = *reinterpret_cast<const float2*>(&Xk[r * D + ca0]);
-            mn0 = v.x < mn0 ? v.x : mn0;
-            mx0 = v.x > mx0 ? v.x : mx0;
-            mn1 = v.y < mn1 ? v.y : mn1;
-            mx1 = v.y > mx1 ? v.y : mx1;
-        }
-        red_mn[part][ca0] = mn0;
-        red_mn[part][ca0 + 1] = mn1;
-        red_mx[part][ca0] = mx0;
-        red_mx[part][ca0 + 1] = mx1;
-        __syncthreads();
-        if (tid < D) {
-            float a = red_mn[0][tid], bmx = red_mx[0][tid];
+        if (kind == 0) {
+            // keys: per channel over the group's stored rows (rows >= nr are padding).  This
+            // thread's rows, then the lanes with the same channels (xor IPR, 2 IPR, ...), then
+            // the waves through LDS.
+            float mn[CH], mx[CH];
 #pragma unroll
-            for (int q = 1; q < KPARTS; ++q) {
-                a = red_mn[q][tid] < a ? red_mn[q][tid] : a;
-                bmx = red_mx[q][tid] > bmx ? red_mx[q][tid] : bmx;
-            }
-            float range = bmx - a;
-            float s = range / 15.0f;
-            s = s + 0.0f;
-            ks[tid] = s;
-            kz[tid] = a + 0.0f;
-        }
-        __syncthreads();
-        const float s0 = ks[ca0], z0 = kz[ca0], s1 = ks[ca0 + 1], z1 = kz[ca0 + 1];
-        const float rs0 = __builtin_amdgcn_rcpf(s0), rs1 = __builtin_amdgcn_rcpf(s1);
-        for (int r = part * KROWS; r < (part + 1) * KROWS; ++r) {
-            uint32_t byte = 0;
-            if (r < nr) {
-                const float2 v = *reinterpret_cast<const float2*>(&Xk[r * D + ca0]);
-                byte = quant_code(v.x, s0, z0, rs0) | (quant_code(v.y, s1, z1, rs1) << 4);
-            }
-            pk[0][r][cp] = (uint8_t)byte;
-        }
-    }
-    // ---- values: per row over each 64-channel group; 8 lanes of 8 channels per (row, group) ----
-    {
-        for (int t = tid; t < 64 * VG * 8; t += 256) {
-            const int sub = t & 7, rg = t >> 3;
-            const int r = rg / VG, gg = rg % VG;
-            const int c0 = gg * 64 + sub * 8;
-            const float4 a = *reinterpret_cast<const float4*>(&Xv[r * XS + c0]);
-            const float4 c = *reinterpret_cast<const float4*>(&Xv[r * XS + c0 + 4]);
-            const float v8[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-            float mn = v8[0], mx = v8[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) {
-                mn = v8[e] < mn ? v8[e] : mn;
-                mx = v8[e] > mx ? v8[e] : mx;
+            for (int c = 0; c < CH; ++c) {
+                mn[c] = __builtin_huge_valf();
+                mx[c] = -__builtin_huge_valf();
             }
 #pragma unroll
-            for (int m = 1; m < 8; m <<= 1) {  // the 8 lanes of this (row, group)
-                mn = fminf(mn, __shfl_xor(mn, m, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, m, 64));
-            }
-            float range = mx - mn;
-            float s = range / 15.0f;
-            s = s + 0.0f;
-            const float z = mn + 0.0f;
-            uint32_t w = 0;
-            if (r < nr) {
-                const float rs = __builtin_amdgcn_rcpf(s);
+            for (int it = 0; it < NIT; ++it) {
+                if ((tid + 256 * it) / IPR >= nr) continue;
 #pragma unroll
-                for (int e = 0; e < 8; e += 2)
-                    w |= (quant_code(v8[e], s, z, rs) | (quant_code(v8[e + 1], s, z, rs) << 4)) << (4 * e);
+                for (int c = 0; c < CH; ++c) {
+                    mn[c] = x[it][c] < mn[c] ? x[it][c] : mn[c];
+                    mx[c] = x[it][c] > mx[c] ? x[it][c] : mx[c];
+                }
             }
-            if (sub == 0) {
-                vs[r][gg] = r < nr ? s : 0.f;
-                vz[r][gg] = r < nr ? z : 0.f;
+#pragma unroll
+            for (int m = IPR; m < 64; m <<= 1)
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    mn[c] = fminf(mn[c], __shfl_xor(mn[c], m, 64));
+                    mx[c] = fmaxf(mx[c], __shfl_xor(mx[c], m, 64));
+                }
+            if (lane < IPR) {
+                *reinterpret_cast<float4*>(&red_mn[wave][c0]) = make_float4(mn[0], mn[1], mn[2], mn[3]);
+                *reinterpret_cast<float4*>(&red_mn[wave][c0 + 4]) = make_float4(mn[4], mn[5], mn[6], mn[7]);
+                *reinterpret_cast<float4*>(&red_mx[wave][c0]) = make_float4(mx[0], mx[1], mx[2], mx[3]);
+                *reinterpret_cast<float4*>(&red_mx[wave][c0 + 4]) = make_float4(mx[4], mx[5], mx[6], mx[7]);
             }
-            *reinterpret_cast<uint32_t*>(&pk[1][r][c0 / 2]) = w;
-        }
-    }
-    __syncthreads();
-
-    // ---- the block: codes of both kinds, key scales/zeros, value meta ----
-    for (int e = tid; e < 2 * 64 * NCP / 16; e += 256) {
-        const int kind = e / (64 * NCP / 16), rest = e % (64 * NCP / 16);
-        const int row = rest / (NCP / 16), byte0 = (rest % (NCP / 16)) * 16;
-        const uint4 w = *reinterpret_cast<const uint4*>(&pk[kind][row][byte0]);
-        *reinterpret_cast<uint4*>(blk + (kind ? Block<D>::vc(row) : Block<D>::kKc + row * (D / 2)) + byte0) = w;
-    }
-    {
-        float* m = reinterpret_cast<float*>(blk + Block<D>::kKm);
-        for (int c = tid; c < D; c += 256) {
-            m[c] = ks[c];
-            m[D + c] = kz[c];
-        }
-        for (int e = tid; e < 64 * VG; e += 256) {
-            float* mv = reinterpret_cast<float*>(blk + Block<D>::vm(e / VG)) + 2 * (e % VG);
-            mv[0] = vs[e / VG][e % VG];
-            mv[1] = vz[e / VG][e % VG];
+            __syncthreads();
+            float s[CH], z[CH], rs[CH];
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                float a = red_mn[0][c0 + c], bmx = red_mx[0][c0 + c];
+#pragma unroll
+                for (int q = 1; q < 4; ++q) {
+                    a = red_mn[q][c0 + c] < a ? red_mn[q][c0 + c] : a;
+                    bmx = red_mx[q][c0 + c] > bmx ? red_mx[q][c0 + c] : bmx;
+                }
+                float range = bmx - a;
+                float sc = range / 15.0f;
+                sc = sc + 0.0f;
+                s[c] = sc;
+                z[c] = a + 0.0f;
+                rs[c] = __builtin_amdgcn_rcpf(sc);
+            }
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int row = (tid + 256 * it) / IPR;
+                uint32_t w = 0;
+                if (row < nr) {
+#pragma unroll
+                    for (int e = 0; e < CH; e += 2)
+                        w |= (quant_code(x[it][e], s[e], z[e], rs[e]) |
+                              (quant_code(x[it][e + 1], s[e + 1], z[e + 1], rs[e + 1]) << 4)) << (4 * e);
+                }
+                *reinterpret_cast<uint32_t*>(blk + Block<D>::kKc + row * (D / 2) + c0 / 2) = w;
+            }
+            if (tid < IPR) {
+                float* m = reinterpret_cast<float*>(blk + Block<D>::kKm) + c0;
+                *reinterpret_cast<float4*>(m) = make_float4(s[0], s[1], s[2], s[3]);
+                *reinterpret_cast<float4*>(m + 4) = make_float4(s[4], s[5], s[6], s[7]);
+                *reinterpret_cast<float4*>(m + D) = make_float4(z[0], z[1], z[2], z[3]);
+                *reinterpret_cast<float4*>(m + D + 4) = make_float4(z[4], z[5], z[6], z[7]);
+            }
+        } else {
+            // values: per row over each 64-channel group, i.e. the 8 lanes (xor 1, 2, 4) whose
+            // items make up the group
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int row = (tid + 256 * it) / IPR;
+                float mn = x[it][0], mx = x[it][0];
+#pragma unroll
+                for (int e = 1; e < CH; ++e) {
+                    mn = x[it][e] < mn ? x[it][e] : mn;
+                    mx = x[it][e] > mx ? x[it][e] : mx;
+                }
+#pragma unroll
+                for (int m = 1; m < 8; m <<= 1) {
+                    mn = fminf(mn, __shfl_xor(mn, m, 64));
+                    mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+                }
+                float range = mx - mn;
+                float sc = range / 15.0f;
+                sc = sc + 0.0f;
+                const float zc = mn + 0.0f;
+                uint32_t w = 0;
+                if (row < nr) {
+                    const float rs = __builtin_amdgcn_rcpf(sc);
+#pragma unroll
+                    for (int e = 0; e < CH; e += 2)
+                        w |= (quant_code(x[it][e], sc, zc, rs) | (quant_code(x[it][e + 1], sc, zc, rs) << 4)) << (4 * e);
+                }
+                *reinterpret_cast<uint32_t*>(blk + Block<D>::vc(row) + c0 / 2) = w;
+                if ((tid & 7) == 0)
+                    *reinterpret_cast<float2*>(blk + Block<D>::vm(row) + (c0 >> 6) * 8) =
+                        make_float2(row < nr ? sc : 0.f, row < nr ? zc : 0.f);
+            }
         }
     }
 
