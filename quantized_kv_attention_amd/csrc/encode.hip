@@ -36,14 +36,14 @@ __device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float 
 // One workgroup encodes one group of up to 64 stored rows of one (sequence, head).  Thread
 // items are 8 channels of one row (one 16-byte load of bf16); for loop r >= 2 each item
 // rebuilds the 8 channels of Xhat^(r-1) through planes 1..r-1 (one code word and its scales
-// per plane; the rows' slots are looked up once per group) and subtracts it.  The residuals
-// stay in registers: keys are quantised per channel over the rows (each thread's rows, then
-// shuffles between the lanes that hold the same channels, then the four waves through LDS),
-// values per row over each 64-channel group (shuffles among the group's 8 lanes), and each
-// thread stores its own code words and metadata into the block.  Three workgroups per CU
-// (at most 168 VGPRs).
+// per plane; the rows' slots are looked up once per group) and subtracts it.  A workgroup
+// encodes one kind, with the residuals in registers: keys are quantised per channel over the
+// rows (each thread's rows, then shuffles between the lanes that hold the same channels, then
+// the four waves through LDS), values per row over each 64-channel group (shuffles among the
+// group's 8 lanes), and each thread stores its own code words and metadata into the block.
+// Four workgroups per CU (at most 128 VGPRs).
 template <int D>
-__global__ __launch_bounds__(256, 3) void encode_group_kernel(CacheArg ca, int loop, int pos0, int n_pos,
+__global__ __launch_bounds__(256, 4) void encode_group_kernel(CacheArg ca, int loop, int pos0, int n_pos,
                                                            const int32_t* __restrict__ act_pos,
                                                            const int32_t* __restrict__ n_act, int ld_act,
                                                            const uint16_t* __restrict__ ksrc,
@@ -53,7 +53,8 @@ __global__ __launch_bounds__(256, 3) void encode_group_kernel(CacheArg ca, int l
     constexpr int IPR = D / CH;          // items per row
     constexpr int NIT = 64 * IPR / 256;  // items per thread
     constexpr int IB = NIT >= 2 ? 2 : 1;  // items whose chain loads go out together
-    const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // keys and values of a group are encoded by two workgroups (they write disjoint parts of the block)
+    const int g = blockIdx.x >> 1, kind = blockIdx.x & 1, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const PlaneArg& P = ca.p[loop - 1];
     const bool dense = P.dense != 0;
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256, 3) void encode_group_kernel(CacheArg ca, int l
     }
     const int lane = tid & 63, wave = tid >> 6;
     const int c0 = (tid % IPR) * CH;  // every item of this thread covers these channels
-    for (int kind = 0; kind < 2; ++kind) {
+    {
         const uint16_t* src = kind ? vsrc : ksrc;
         const uint16_t* tail = kind ? ca.tail_v[loop - 1] : ca.tail_k[loop - 1];
         float x[NIT][CH];
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(256, 3) void encode_group_kernel(CacheArg ca, int l
         }
     }
 
-    if (!dense && h == 0 && tid < 64)
+    if (!dense && h == 0 && kind == 0 && tid < 64)
         rowpos[(size_t)b * P.n_blocks * 64 + base + r0 + tid] = spos[tid];
 }
 
@@ -364,7 +365,7 @@ int launch_encode(const CacheArg& ca, int D, int loop, int pos0, int n_pos, cons
                   hipStream_t st) {
     const PlaneArg& P = ca.p[loop - 1];
     const int ngroups = (n_pos + 63) / 64;
-    dim3 grid(ngroups, ca.H, ca.B);
+    dim3 grid(2 * ngroups, ca.H, ca.B);  // a key and a value workgroup per group
     int32_t* rowpos = const_cast<int32_t*>(P.rowpos);
     const size_t dyn = (size_t)(loop - 1) * 64 * sizeof(int);  // chain slots of the stored rows
     if (D == 128)
