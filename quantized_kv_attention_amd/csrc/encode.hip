@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256, 4) void encode_group_kernel(CacheArg ca, int l
             if (ipos[it] >= 0) {
                 const uint16_t* rp = from_tail ? tail + (bh * kTail + (ipos[it] % kTail)) * D + c0
                                                : src + (bh * ld_src + r0 + row) * D + c0;
-                bf16x8(*reinterpret_cast<const uint4*>(rp), x[it]);
+                bf16x8(ld_stream_u4(rp), x[it]);
             }
         }
         if (nch > 0) {

@@ -209,14 +209,14 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 1) void sparse_chunk_ke
                         const int slot = act[u] ? sl[u] : 0;
                         const uint8_t* bp = block_ptr<D>(P, ca.H, b, h, slot >> 6);
                         const int row = slot & 63;
-                        kw[u] = *reinterpret_cast<const uint32_t*>(bp + Block<D>::kKc + row * (D / 2) + prt * 4);
-                        vw[u] = *reinterpret_cast<const uint32_t*>(bp + Block<D>::vc(row) + prt * 4);
+                        kw[u] = ld_stream_u32(bp + Block<D>::kKc + row * (D / 2) + prt * 4);
+                        vw[u] = ld_stream_u32(bp + Block<D>::vc(row) + prt * 4);
                         const float* km = reinterpret_cast<const float*>(bp + Block<D>::kKm) + c0;
                         s0[u] = *reinterpret_cast<const float4*>(km);
                         s1[u] = *reinterpret_cast<const float4*>(km + 4);
                         z0[u] = *reinterpret_cast<const float4*>(km + D);
                         z1[u] = *reinterpret_cast<const float4*>(km + D + 4);
-                        vm[u] = *reinterpret_cast<const float2*>(bp + Block<D>::vm(row) + (c0 >> 6) * 8);
+                        vm[u] = ld_stream_f2(bp + Block<D>::vm(row) + (c0 >> 6) * 8);
                     }
 #pragma unroll
                     for (int u = 0; u < SB; ++u) {
@@ -266,14 +266,14 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 1) void sparse_chunk_ke
                         if (slot < 0 || slot >= P.n_blocks * 64) continue;
                         const uint8_t* bp = block_ptr<D>(P, ca.H, b, h, slot >> 6);
                         const int row = slot & 63;
-                        const uint32_t kw = *reinterpret_cast<const uint32_t*>(bp + Block<D>::kKc + row * (D / 2) + prt * 4);
-                        const uint32_t vw = *reinterpret_cast<const uint32_t*>(bp + Block<D>::vc(row) + prt * 4);
+                        const uint32_t kw = ld_stream_u32(bp + Block<D>::kKc + row * (D / 2) + prt * 4);
+                        const uint32_t vw = ld_stream_u32(bp + Block<D>::vc(row) + prt * 4);
                         const float* km = reinterpret_cast<const float*>(bp + Block<D>::kKm) + c0;
                         const float4 s0 = *reinterpret_cast<const float4*>(km);
                         const float4 s1 = *reinterpret_cast<const float4*>(km + 4);
                         const float4 z0 = *reinterpret_cast<const float4*>(km + D);
                         const float4 z1 = *reinterpret_cast<const float4*>(km + D + 4);
-                        const float2 vm = *reinterpret_cast<const float2*>(bp + Block<D>::vm(row) + (c0 >> 6) * 8);
+                        const float2 vm = ld_stream_f2(bp + Block<D>::vm(row) + (c0 >> 6) * 8);
                         const float ks[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
                         const float kz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
                         float code[8];

@@ -1,5 +1,6 @@
-// Plain streaming read: the bandwidth a read with nothing else to do reaches on the device,
-// set beside the readers' rates.  Not part of the attention path.
+// Plain streaming read: the bandwidth a read with nothing else to do reaches on the device
+// (with the readers' nontemporal load policy), set beside the readers' rates.  Not part of
+// the attention path.
 #include "launch.h"
 
 namespace qkv {
@@ -18,7 +19,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4
 #pragma unroll
         for (int u = 0; u < kStreamUnroll; ++u) {
             const size_t i = t0 + (size_t)u * kStreamThreads + threadIdx.x;
-            v[u] = i < n16 ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+            v[u] = i < n16 ? ld_stream_u4(src + i) : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
