@@ -98,7 +98,8 @@ __device__ __forceinline__ void vpass_block(const uint8_t* bp, int prt, int rsub
 // NPRE (1 or 2): leading dense planes whose blocks are read together, with their folded
 // queries prepared once per split; later planes (sparse, or dense beyond NPRE) follow one
 // by one.  Three waves per SIMD (the plan's three workgroups per CU) leave up to 168 VGPRs
-// per wave: the two-plane kernel needs ~154, and under a 128 cap it spilled to scratch.
+// per wave.  With its plane loads on the streaming policy the two-plane kernel compiles to
+// 128, but four workgroups per CU made the decode step slower.
 template <int D, int NPRE>
 __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                           NewRow nr, float sm, float* __restrict__ scores, int ld,
