@@ -18,6 +18,8 @@ def test_ctx32k_sampled_heads():
     compare_planes(p.gpu, p.orc, [0, 11], [0, 1])
     say("ctx32k: decode step")
     check_step(p, p.queries(0), w.n_dense, w.k_cols(w.n), "ctx32k")
+    say("ctx32k: every loop read densely through its full chain (the bench's comparison row)")
+    check_step(p, p.queries(0), w.R, 0, "ctx32k full chain")
 
 
 def test_ctx4k_64_decode_steps_with_flush():
