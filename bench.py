@@ -151,8 +151,10 @@ def main():
                 stack.select(loop, k)    # loop `loop`'s selections of every layer in one call
             for ly in layers:
                 # the call stores this loop's row of the new token (position n) in the tail
+                # (a dense loop before the last dense one stores no raw scores: the next overwrites them)
                 qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k, selected=batched,
-                                   k_new=ly["kn"][loop - 1], v_new=ly["vn"][loop - 1])
+                                   k_new=ly["kn"][loop - 1], v_new=ly["vn"][loop - 1],
+                                   need_scores=loop >= w.n_dense)
 
     def dense2():
         for ly in layers:
@@ -241,7 +243,8 @@ def main():
         lb = 0
         if r < w.n_dense:
             for b in range(B):
-                lb += H * bm.dense_loop_bytes([rows[p][b] for p in range(r + 1)], T, n_step, d)
+                lb += H * bm.dense_loop_bytes([rows[p][b] for p in range(r + 1)], T, n_step, d,
+                                              scores=r + 1 >= w.n_dense)
         else:
             # the selection loop r made in the last replay
             idx_all = b0.selection(r + 1, k)[0].cpu().numpy()
@@ -411,7 +414,8 @@ def measure_rows(w, layers, stack, dense, n, nb, k, loop_bytes, flush_loop_bytes
     # dense loops (every loop the configuration runs densely), selection, sparse loops
     for loop in range(1, w.R + 1):
         if loop <= w.n_dense:
-            t = timed(lambda: [qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k)
+            t = timed(lambda: [qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k,
+                                                  need_scores=loop >= w.n_dense)
                                for ly in layers])
             out[f"attn_decode_dense loop {loop}"] = row(t, L, loop_bytes[loop - 1])
         else:

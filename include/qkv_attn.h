@@ -167,7 +167,8 @@ int kv_append_tail(const qkv_cache* cache, int loop, int pos0, int n_rows,
  *            1, k_new, v_new) would, and attends over them in the same launch
  *            [PyPI Configuration: 64-token BF16 residual tail].
  *   o        device bf16 [batch][heads][head_dim] (may be NULL); o_f32 device fp32 same shape.
- *   scores   device fp32 [batch][heads][ld_scores]: raw logits s_j, j < n_ctx.
+ *   scores   device fp32 [batch][heads][ld_scores]: raw logits s_j, j < n_ctx; or NULL when
+ *            no later call reads them (ld_scores is then ignored).
  *   lse      device fp32 [batch][heads]: log sum_j exp(s_j).
  */
 int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,

@@ -137,7 +137,8 @@ def attn_decode_dense(cache, loop, q, sm_scale, o, o_f32, scores, lse, ws, strea
     in the loop's tail by the same call; None when the tail already holds it."""
     st = lib().attn_decode_dense(ctypes.byref(cache.desc), loop, _ptr(q), _ptr(k_new), _ptr(v_new), float(sm_scale),
                                  _ptr(o), _ptr(o_f32),
-                                 _ptr(scores), scores.shape[-1], _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _ptr(scores), 0 if scores is None else scores.shape[-1], _ptr(lse), _ptr(ws),
+                                 ws.numel() * ws.element_size(),
                                  _stream(stream))
     _check("attn_decode_dense", st)
 

@@ -19,12 +19,13 @@ def plane_bytes(rows: int, d: int) -> int:
     return rows * d + groups * d * 8 + rows * (d // GROUP) * 8
 
 
-def dense_loop_bytes(rows_per_plane, tail_rows: int, n: int, d: int) -> int:
-    """Dense loop r for one (sequence, head): planes 1..r, the loop's BF16 tail, q, scores, o."""
+def dense_loop_bytes(rows_per_plane, tail_rows: int, n: int, d: int, scores: bool = True) -> int:
+    """Dense loop r for one (sequence, head): planes 1..r, the loop's BF16 tail, q, scores
+    (unless the loop does not store them), o."""
     b = sum(plane_bytes(r, d) for r in rows_per_plane)
     b += tail_rows * d * 2 * 2          # BF16 K and V rows of the tail
     b += d * 2                          # query
-    b += n * 4                          # raw scores written for the next selection
+    b += n * 4 if scores else 0         # raw scores written for the next selection
     b += d * (2 + 4) + 4                # o (bf16 + fp32) and lse
     return b
 

@@ -259,18 +259,20 @@ def k_columns(frac: float, n: int) -> int:
 
 
 def decode_loop(cache: LayerCache, bufs: DecodeBuffers, loop: int, q, n_dense: int, k: int, sm: float = 1.0,
-                stream=None, selected: bool = False, k_new=None, v_new=None):
+                stream=None, selected: bool = False, k_new=None, v_new=None, need_scores: bool = True):
     """Attention of loop `loop` (1-based) for query q [B, H, d] bf16.
 
     A sparse loop first selects its k columns from the previous loop's scores, unless
     `selected` says that the selection is already in place (LayerStack.select).
     k_new / v_new ([B, H, d] bf16): this loop's row of the newest position, stored in the
-    loop's tail by the attention call itself (after LayerCache.advance_token)."""
+    loop's tail by the attention call itself (after LayerCache.advance_token).
+    need_scores=False: a dense loop does not store its raw scores (when the next loop is
+    dense too and overwrites them)."""
     r = loop - 1
     main = torch.cuda.current_stream() if stream is None else stream
     if loop <= n_dense:
-        attn_decode_dense(cache, loop, q, sm, bufs.o[r], bufs.o_f32[r], bufs.scores, bufs.lse, bufs.ws, main,
-                          k_new=k_new, v_new=v_new)
+        attn_decode_dense(cache, loop, q, sm, bufs.o[r], bufs.o_f32[r], bufs.scores if need_scores else None,
+                          bufs.lse, bufs.ws, main, k_new=k_new, v_new=v_new)
     else:
         assert k <= bufs.max_k
         idx, ps, mass = bufs.selection(loop, k)
@@ -283,11 +285,13 @@ def decode_loop(cache: LayerCache, bufs: DecodeBuffers, loop: int, q, n_dense: i
 def decode_step(cache: LayerCache, bufs: DecodeBuffers, q, n_dense: int, k: int, sm: float = 1.0, stream=None,
                 k_new=None, v_new=None):
     """All loops of one decode step of one layer; q[r] bf16 [B, H, d].  With k_new / v_new
-    (per loop, [B, H, d] bf16) each loop's call stores its row of the newest position."""
+    (per loop, [B, H, d] bf16) each loop's call stores its row of the newest position.  Dense
+    loops before the last dense one do not store raw scores: the next loop overwrites them."""
     for loop in range(1, cache.R + 1):
         kn = None if k_new is None else k_new[loop - 1]
         vn = None if v_new is None else v_new[loop - 1]
-        decode_loop(cache, bufs, loop, q[loop - 1], n_dense, k, sm, stream, k_new=kn, v_new=vn)
+        decode_loop(cache, bufs, loop, q[loop - 1], n_dense, k, sm, stream, k_new=kn, v_new=vn,
+                    need_scores=loop >= n_dense)
 
 
 def decode_step_stack(stack: LayerStack, qs, n_dense: int, k: int, sm: float = 1.0, stream=None,
@@ -302,4 +306,5 @@ def decode_step_stack(stack: LayerStack, qs, n_dense: int, k: int, sm: float = 1
         for l, (c, b) in enumerate(zip(stack.caches, stack.layers)):
             kn = None if k_new is None else k_new[l][loop - 1]
             vn = None if v_new is None else v_new[l][loop - 1]
-            decode_loop(c, b, loop, qs[l][loop - 1], n_dense, k, sm, main, selected=True, k_new=kn, v_new=vn)
+            decode_loop(c, b, loop, qs[l][loop - 1], n_dense, k, sm, main, selected=True, k_new=kn, v_new=vn,
+                        need_scores=loop >= n_dense)

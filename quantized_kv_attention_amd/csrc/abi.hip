@@ -147,7 +147,7 @@ int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, const
     if (st) return st;
     if (loop < 1 || loop > cache->n_loops) return QKV_EINVAL;
     if (cache->n_ctx < 1) return QKV_EINVAL;
-    if (!q || !o_f32 || !scores || !lse || ld_scores < cache->n_ctx) return QKV_EINVAL;
+    if (!q || !o_f32 || !lse || (scores && ld_scores < cache->n_ctx)) return QKV_EINVAL;
     if (!aligned16(q) || !aligned16(o_f32) || (o && !aligned16(o))) return QKV_EINVAL;
     if ((k_new == nullptr) != (v_new == nullptr) || (k_new && (!aligned16(k_new) || !aligned16(v_new))))
         return QKV_EINVAL;

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
     };
     for (int c = tid; c < D; c += 256) qsh[c] = bf16_to_f32(q[(size_t)bh * D + c]) * sm;
     float* out = part + ((size_t)bh * nsplit + s) * (D + 2);
-    float* srow = scores + (size_t)bh * ld;
+    float* srow = scores ? scores + (size_t)bh * ld : nullptr;  // null: raw scores not stored
 
     float acc[32];
 #pragma unroll
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
         load_v(blkP);
         float lm = -__builtin_huge_valf();
         for (int i = tid; i < L + T; i += 256) {
-            srow[j0 + i] = logit[i];   // the tail rows follow the split's body rows (j0 + L == n_body)
+            if (srow) srow[j0 + i] = logit[i];  // the tail rows follow the split's body rows (j0 + L == n_body)
             lm = fmaxf(lm, logit[i]);
         }
         mx = block_reduce_max(lm, red);

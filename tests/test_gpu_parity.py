@@ -160,3 +160,31 @@ def test_special_values_codes():
     o.prefill(K, V, act)
     torch.cuda.synchronize()
     compare_planes(g, o, [0], [0])
+
+
+def test_dense_loop_without_scores():
+    # a dense call given no score buffer: the same o, o_f32 and lse bit for bit, and the
+    # score buffer left as it was; the step that skips loop 1's scores ends equal too
+    w = dataclasses.replace(W["ctx4k"], H=3)
+    p = Pair(w, n=1500, extra=8)
+    q = [to_dev_bf16(x) for x in p.queries(2)]
+    c, b = p.gpu, p.bufs
+    qcache.decode_loop(c, b, 1, q[0], w.n_dense, 0)
+    torch.cuda.synchronize()
+    ref = [b.o[0].clone(), b.o_f32[0].clone(), b.lse.clone()]
+    b.scores.fill_(7.0)
+    b.o_f32[0].zero_()
+    qcache.decode_loop(c, b, 1, q[0], w.n_dense, 0, need_scores=False)
+    torch.cuda.synchronize()
+    assert torch.equal(b.o[0], ref[0]) and torch.equal(b.o_f32[0], ref[1]) and torch.equal(b.lse, ref[2])
+    assert bool((b.scores == 7.0).all())
+    k = w.k_cols(c.n_ctx)
+    outs = []
+    for skip in (False, True):
+        for loop in range(1, w.R + 1):
+            qcache.decode_loop(c, b, loop, q[loop - 1], w.n_dense, k,
+                               need_scores=(loop >= w.n_dense) if skip else True)
+        torch.cuda.synchronize()
+        outs.append([b.o_f32[r].clone() for r in range(w.R)] + [b.scores.clone(), b.lse.clone()])
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
