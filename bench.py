@@ -151,10 +151,10 @@ def main():
                 stack.select(loop, k)    # loop `loop`'s selections of every layer in one call
             for ly in layers:
                 # the call stores this loop's row of the new token (position n) in the tail
-                # (a dense loop before the last dense one stores no raw scores: the next overwrites them)
+                # (a loop stores scores only when the next loop selects from them)
                 qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k, selected=batched,
                                    k_new=ly["kn"][loop - 1], v_new=ly["vn"][loop - 1],
-                                   need_scores=loop >= w.n_dense)
+                                   need_scores=qcache.scores_read_after(loop, w.n_dense, w.R))
 
     def dense2():
         for ly in layers:
@@ -244,14 +244,15 @@ def main():
         if r < w.n_dense:
             for b in range(B):
                 lb += H * bm.dense_loop_bytes([rows[p][b] for p in range(r + 1)], T, n_step, d,
-                                              scores=r + 1 >= w.n_dense)
+                                              scores=qcache.scores_read_after(r + 1, w.n_dense, w.R))
         else:
             # the selection loop r made in the last replay
             idx_all = b0.selection(r + 1, k)[0].cpu().numpy()
             lb += B * H * bm.select_bytes(n_step, k)
             for b in range(B):
                 for h in range(H):
-                    lb += bm.sparse_loop_bytes(idx_all[b, h], [slots[p][b] for p in range(r + 1)], nb, d)
+                    lb += bm.sparse_loop_bytes(idx_all[b, h], [slots[p][b] for p in range(r + 1)], nb, d,
+                                               scores=qcache.scores_read_after(r + 1, w.n_dense, w.R))
         loop_bytes.append(lb)
         step_bytes += lb
     append_bytes = w.R * B * H * d * 2 * 2 * 2               # read new K/V, write the tail rows
@@ -415,7 +416,7 @@ def measure_rows(w, layers, stack, dense, n, nb, k, loop_bytes, flush_loop_bytes
     for loop in range(1, w.R + 1):
         if loop <= w.n_dense:
             t = timed(lambda: [qcache.decode_loop(ly["c"], ly["b"], loop, ly["q"][loop - 1], w.n_dense, k,
-                                                  need_scores=loop >= w.n_dense)
+                                                  need_scores=qcache.scores_read_after(loop, w.n_dense, w.R))
                                for ly in layers])
             out[f"attn_decode_dense loop {loop}"] = row(t, L, loop_bytes[loop - 1])
         else:
@@ -430,7 +431,9 @@ def measure_rows(w, layers, stack, dense, n, nb, k, loop_bytes, flush_loop_bytes
             def sp(ly):
                 idx, ps, mass = ly["b"].selection(loop, k)
                 qkv.attn_decode_sparse(ly["c"], loop, ly["q"][loop - 1], 1.0, idx, ps, mass, k,
-                                       ly["b"].o_f32[loop - 2], ly["b"].lse, ly["b"].scores, ly["b"].o[loop - 1],
+                                       ly["b"].o_f32[loop - 2], ly["b"].lse,
+                                       ly["b"].scores if qcache.scores_read_after(loop, w.n_dense, w.R) else None,
+                                       ly["b"].o[loop - 1],
                                        ly["b"].o_f32[loop - 1], ly["b"].ws, s)
             t = timed(lambda: [sp(ly) for ly in layers])
             sel_b = w.B * w.H * bm.select_bytes(n + 1, k)

@@ -201,6 +201,8 @@ int select_columns(const float* scores, int ld_scores, const float* lse, int bat
  *   0 <= k <= n_ctx (k == 0: o = o_prev).
  *   o_prev   device fp32 [batch][heads][head_dim]: previous loop's output (full precision).
  *   lse      device fp32 [batch][heads]: the lse the selection used.
+ *   scores   as for attn_decode_dense, updated in place; or NULL when no later selection
+ *            reads them (the splice is then not stored, ld_scores ignored).
  *   k_new, v_new  as for attn_decode_dense: loop `loop`'s row of the newest position,
  *            stored in the loop's tail and used for that column if it is selected (its
  *            loop-(loop-1) value is read from that loop's tail, written by its own call).

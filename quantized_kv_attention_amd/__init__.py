@@ -157,7 +157,8 @@ def attn_decode_sparse(cache, loop, q, sm_scale, idx, p_sel, mass, k, o_prev, ls
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     st = lib().attn_decode_sparse(ctypes.byref(cache.desc), loop, _ptr(q), _ptr(k_new), _ptr(v_new), float(sm_scale),
                                   _ptr(idx), _ptr(p_sel),
-                                  _ptr(mass), k, _ptr(o_prev), _ptr(lse), _ptr(scores), scores.shape[-1], _ptr(o),
+                                  _ptr(mass), k, _ptr(o_prev), _ptr(lse), _ptr(scores),
+                                  0 if scores is None else scores.shape[-1], _ptr(o),
                                   _ptr(o_f32), _ptr(ws), wsb, _stream(stream))
     _check("attn_decode_sparse", st)
 

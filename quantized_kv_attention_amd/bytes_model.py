@@ -41,7 +41,7 @@ def select_bytes(n: int, k: int) -> int:
     return n * 4 + 4 + k * 8 + 4        # scores + lse in; idx + p_sel + mass out
 
 
-def sparse_loop_bytes(idx: np.ndarray, slots_per_plane, n_body: int, d: int) -> int:
+def sparse_loop_bytes(idx: np.ndarray, slots_per_plane, n_body: int, d: int, scores: bool = True) -> int:
     """Sparse loop r for one (sequence, head).
 
     idx: selected columns (ascending).  slots_per_plane[p]: int array over body positions
@@ -58,7 +58,7 @@ def sparse_loop_bytes(idx: np.ndarray, slots_per_plane, n_body: int, d: int) -> 
         b += np.unique(s // GROUP).size * d * 8      # K metadata of each touched key group
     b += ntail * d * 2 * 3                          # tail K^(r), V^(r), V^(r-1)
     b += idx.size * (4 + 4)                         # idx, p_sel
-    b += idx.size * (4 + 4)                         # score written, then shifted in place
+    b += idx.size * (4 + 4) if scores else 0        # score written, then shifted in place
     b += d * 2 + d * 4 + d * (2 + 4) + 4 + 4       # q, o_prev, o (bf16 + fp32), mass, lse
     return b
 

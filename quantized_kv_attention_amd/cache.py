@@ -266,8 +266,8 @@ def decode_loop(cache: LayerCache, bufs: DecodeBuffers, loop: int, q, n_dense: i
     `selected` says that the selection is already in place (LayerStack.select).
     k_new / v_new ([B, H, d] bf16): this loop's row of the newest position, stored in the
     loop's tail by the attention call itself (after LayerCache.advance_token).
-    need_scores=False: a dense loop does not store its raw scores (when the next loop is
-    dense too and overwrites them)."""
+    need_scores=False: the loop stores no scores (a dense loop whose next loop is dense too
+    and overwrites them; the last loop, whose scores no selection reads)."""
     r = loop - 1
     main = torch.cuda.current_stream() if stream is None else stream
     if loop <= n_dense:
@@ -278,20 +278,26 @@ def decode_loop(cache: LayerCache, bufs: DecodeBuffers, loop: int, q, n_dense: i
         idx, ps, mass = bufs.selection(loop, k)
         if not selected:
             select_columns(bufs.scores, bufs.lse, cache.n_ctx, k, idx, ps, mass, None, main)
-        attn_decode_sparse(cache, loop, q, sm, idx, ps, mass, k, bufs.o_f32[r - 1], bufs.lse, bufs.scores,
-                           bufs.o[r], bufs.o_f32[r], bufs.ws, main, k_new=k_new, v_new=v_new)
+        attn_decode_sparse(cache, loop, q, sm, idx, ps, mass, k, bufs.o_f32[r - 1], bufs.lse,
+                           bufs.scores if need_scores else None, bufs.o[r], bufs.o_f32[r], bufs.ws, main,
+                           k_new=k_new, v_new=v_new)
+
+
+def scores_read_after(loop: int, n_dense: int, n_loops: int) -> bool:
+    """Whether a selection reads loop `loop`'s scores: those of the next loop, if it is sparse."""
+    return n_dense <= loop < n_loops
 
 
 def decode_step(cache: LayerCache, bufs: DecodeBuffers, q, n_dense: int, k: int, sm: float = 1.0, stream=None,
                 k_new=None, v_new=None):
     """All loops of one decode step of one layer; q[r] bf16 [B, H, d].  With k_new / v_new
-    (per loop, [B, H, d] bf16) each loop's call stores its row of the newest position.  Dense
-    loops before the last dense one do not store raw scores: the next loop overwrites them."""
+    (per loop, [B, H, d] bf16) each loop's call stores its row of the newest position.  A loop
+    stores scores only when the next loop selects from them."""
     for loop in range(1, cache.R + 1):
         kn = None if k_new is None else k_new[loop - 1]
         vn = None if v_new is None else v_new[loop - 1]
         decode_loop(cache, bufs, loop, q[loop - 1], n_dense, k, sm, stream, k_new=kn, v_new=vn,
-                    need_scores=loop >= n_dense)
+                    need_scores=scores_read_after(loop, n_dense, cache.R))
 
 
 def decode_step_stack(stack: LayerStack, qs, n_dense: int, k: int, sm: float = 1.0, stream=None,
@@ -307,4 +313,4 @@ def decode_step_stack(stack: LayerStack, qs, n_dense: int, k: int, sm: float = 1
             kn = None if k_new is None else k_new[l][loop - 1]
             vn = None if v_new is None else v_new[l][loop - 1]
             decode_loop(c, b, loop, qs[l][loop - 1], n_dense, k, sm, main, selected=True, k_new=kn, v_new=vn,
-                        need_scores=loop >= n_dense)
+                        need_scores=scores_read_after(loop, n_dense, stack.caches[0].R))

@@ -176,7 +176,7 @@ int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, cons
     if (st) return st;
     if (loop < 2 || loop > cache->n_loops) return QKV_EINVAL;
     if (cache->n_ctx < 1 || k < 0 || k > cache->n_ctx) return QKV_EINVAL;
-    if (!q || !o_prev || !lse || !scores || !o_f32 || ld_scores < cache->n_ctx) return QKV_EINVAL;
+    if (!q || !o_prev || !lse || !o_f32 || (scores && ld_scores < cache->n_ctx)) return QKV_EINVAL;
     if (k > 0 && (!idx || !p_sel || !mass)) return QKV_EINVAL;
     if (!aligned16(q) || (o && !aligned16(o))) return QKV_EINVAL;
     if ((k_new == nullptr) != (v_new == nullptr) || (k_new && (!aligned16(k_new) || !aligned16(v_new))))

@@ -308,7 +308,7 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 1) void sparse_chunk_ke
         for (int c = 0; c < 8; ++c) s = fmaf(qv[c], kh[c], s);
         s = lane_group_sum<LPC>(s);
         if (!valid) s = -__builtin_huge_valf();
-        else if (prt == 0) cs[(size_t)bh * k + i] = s;  // raw score of entry i; the combine shifts it
+        else if (prt == 0 && cs) cs[(size_t)bh * k + i] = s;  // raw score of entry i; the combine shifts it
         const float nm = fmaxf(mxw, wave_max(s));
         const float scale = (mxw == -__builtin_huge_valf()) ? 0.f : __expf(mxw - nm);
         const float e = valid ? __expf(s - nm) : 0.f;
@@ -444,17 +444,19 @@ __global__ __launch_bounds__(64 * kSpCombineWaves) void sparse_combine_kernel(
     __shared__ __align__(16) float red[kSpCombineWaves * 2 * D];
     // the selected columns and their raw scores (entry order), the mass, the previous lse
     // and output: none depends on the merge, so all go out with the partials
+    // (no score buffer: the splice is not stored)
     constexpr int kPre = 4;
-    float* srow = scores + (size_t)bh * ld;
+    const bool splice = scores != nullptr;
+    float* srow = splice ? scores + (size_t)bh * ld : nullptr;
     const int32_t* id = idx + (size_t)bh * k;
-    const float* cr = cs + (size_t)bh * k;
+    const float* cr = splice ? cs + (size_t)bh * k : nullptr;
     int jv[kPre];
     float sv[kPre];
 #pragma unroll
     for (int e = 0; e < kPre; ++e) {
         const int i = tid + e * NT;
-        jv[e] = i < k ? id[i] : -1;
-        sv[e] = i < k ? cr[i] : 0.f;
+        jv[e] = splice && i < k ? id[i] : -1;
+        sv[e] = splice && i < k ? cr[i] : 0.f;
     }
     const float m = mass[bh], lse_prev = lse[bh];
     const float op = tid < D ? o_prev[(size_t)bh * D + tid] : 0.f;
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(64 * kSpCombineWaves) void sparse_combine_kernel(
 #pragma unroll
     for (int e = 0; e < kPre; ++e)
         if (jv[e] >= 0 && jv[e] < ld) srow[jv[e]] = sv[e] + shift;
-    for (int i = tid + kPre * NT; i < k; i += NT) {
+    for (int i = tid + kPre * NT; splice && i < k; i += NT) {
         const int j = id[i];
         if (j >= 0 && j < ld) srow[j] = cr[i] + shift;
     }
@@ -515,7 +517,7 @@ int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow
         return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
     }
     float* part = static_cast<float*>(ws);
-    float* cs = part + (size_t)ca.B * ca.H * nchunk * sp_record(D);
+    float* cs = scores ? part + (size_t)ca.B * ca.H * nchunk * sp_record(D) : nullptr;  // raw scores for the splice
     dim3 grid(nchunk, ca.H, ca.B);
     // deep chains: batched loads (and long chains first), which need every plane of the
     // chain to hold a block

@@ -188,3 +188,22 @@ def test_dense_loop_without_scores():
         outs.append([b.o_f32[r].clone() for r in range(w.R)] + [b.scores.clone(), b.lse.clone()])
     for x, y in zip(*outs):
         assert torch.equal(x, y)
+
+
+def test_sparse_loop_without_scores():
+    # a sparse call given no score buffer: the same o and o_f32 bit for bit, scores untouched
+    w = dataclasses.replace(W["ctx4k"], H=3)
+    p = Pair(w, n=1500, extra=8)
+    q = [to_dev_bf16(x) for x in p.queries(4)]
+    c, b = p.gpu, p.bufs
+    k = w.k_cols(c.n_ctx)
+    for loop in range(1, w.n_dense + 2):
+        qcache.decode_loop(c, b, loop, q[loop - 1], w.n_dense, k)
+    torch.cuda.synchronize()
+    r = w.n_dense  # the sparse loop just run, 0-based
+    ref = [b.o[r].clone(), b.o_f32[r].clone()]
+    saved = b.scores.clone()
+    qcache.decode_loop(c, b, w.n_dense + 1, q[w.n_dense], w.n_dense, k, selected=True, need_scores=False)
+    torch.cuda.synchronize()
+    assert torch.equal(b.o[r], ref[0]) and torch.equal(b.o_f32[r], ref[1])
+    assert torch.equal(b.scores, saved)
