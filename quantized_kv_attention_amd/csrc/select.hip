@@ -25,6 +25,7 @@ constexpr int kSelPerThread = 40;      // register-resident scores per thread (n
 constexpr int kBins = 2048;
 constexpr int kCandCap = 2048;         // threshold-bin columns ranked exactly
 constexpr int kStage = 4096;           // selections staged in LDS for coalesced stores
+constexpr uint32_t kNoBin = 0xFFFFFFFFu;  // no threshold bin found
 
 __device__ __forceinline__ uint32_t order_key(float x) {
     uint32_t u = __float_as_uint(x);
@@ -42,10 +43,13 @@ __device__ __forceinline__ uint64_t sort_word(float x, int j) {
     return ((uint64_t)order_key(x) << 32) | (uint64_t)(~(uint32_t)j);
 }
 
-// Bin of a score x >= lo in [0, kBins) (off = -lo * scale); -inf (a column past n) gets
-// bin -1.  Monotone in x, which is all the selection needs of it.
-__device__ __forceinline__ int value_bin(float x, float scale, float off) {
-    return (int)__builtin_amdgcn_fmed3f(fmaf(x, scale, off), -1.f, (float)(kBins - 1));
+// Bin of a score x >= lo in [0, kBins); -inf (a column past n) gets bin -1.  The difference
+// x - lo of two fp32 values x >= lo rounds to a value >= +0, so every finite score lands in
+// [0, kBins) however far the scores sit from zero (a bias folded into one FMA, -lo * scale,
+// is itself rounded and sent scores near lo to bin -1 once |lo| / (hi - lo) reached ~8192).
+// Rounding is monotone, so the bin is monotone in x, which is all the selection needs of it.
+__device__ __forceinline__ int value_bin(float x, float lo, float scale) {
+    return (int)__builtin_amdgcn_fmed3f((x - lo) * scale, -1.f, (float)(kBins - 1));
 }
 
 __device__ __forceinline__ uint64_t lanes_below() {
@@ -222,7 +226,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
             fmin_sh[wave] = mn;
             fmax_sh[wave] = mx;
         }
-        if (tid == 0) bcast[2] = 0;  // candidate count
+        if (tid == 0) {
+            bcast[0] = kNoBin;  // stays so only if the histogram misses the k-th column
+            bcast[2] = 0;       // candidate count
+            thr_unique = 0u;    // stays 0 unless the ranking finds the threshold column
+        }
 #pragma unroll
         for (int e = 0; e < kSelPerThread; ++e) v[e] = e * kSelThreads + tid < n ? v[e] : kNegInf;
         __syncthreads();
@@ -234,11 +242,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
         }
         const float range = hi - lo;
         const float scale = (float)kBins / range;
-        const float boff = -lo * scale;
         if (range > 0.f && __builtin_isfinite(range) && __builtin_isfinite(scale)) {
 #pragma unroll
             for (int e = 0; e < kSelPerThread; ++e)
-                if (v[e] > kNegInf) atomicAdd(&hist[value_bin(v[e], scale, boff)], 1u);
+                if (v[e] > kNegInf) atomicAdd(&hist[value_bin(v[e], lo, scale)], 1u);
             __syncthreads();
             // bin of the k-th largest, counting from the top bin (thread t: bins 2047-2t, 2046-2t)
             const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
@@ -255,11 +262,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
             __syncthreads();
             const int bstar = (int)bcast[0];
             const uint32_t need_in = (uint32_t)k - bcast[1];  // columns taken inside the threshold bin
-            if (hist[bstar] <= (uint32_t)kCandCap) {
+            // every column of the fast path is finite and binned, so the k-th is always found;
+            // should it not be, the memory paths decide
+            if (bcast[0] != kNoBin && hist[bstar] <= (uint32_t)kCandCap) {
                 // the threshold bin's columns as (key, index) sort words
 #pragma unroll
                 for (int e = 0; e < kSelPerThread; ++e) {
-                    if (value_bin(v[e], scale, boff) == bstar) {  // never for -inf (bin -1)
+                    if (value_bin(v[e], lo, scale) == bstar) {  // never for -inf (bin -1)
                         const uint32_t slot = atomicAdd(&bcast[2], 1u);
                         cand[slot] = sort_word(v[e], e * kSelThreads + tid);
                     }

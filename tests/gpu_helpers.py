@@ -165,6 +165,9 @@ def check_step(pair: Pair, q, n_dense, k, label=""):
     B, H = oc.B, oc.H
     # untaught oracle step
     ref = oc.step(q, n_dense=n_dense, k=k, threads=8)
+    # (b, h) whose selections so far equal the untaught oracle's (their selection inputs agree)
+    same = np.ones((B, H), bool)
+    gapped = 0
     for r in range(oc.R):
         s = snaps[r]
         if r < n_dense:
@@ -182,7 +185,8 @@ def check_step(pair: Pair, q, n_dense, k, label=""):
                     assert np.array_equal(s["idx"][b, h], idx), f"{label} loop {r + 1} idx b={b} h={h}"
                     np.testing.assert_allclose(s["p_sel"][b, h], p, rtol=1e-5, atol=1e-30)
                     assert abs(s["mass"][b, h] - m) <= 1e-5 * max(m, 1e-30)
-        # teacher-forced splice: the oracle takes the GPU's selection, mass and o_prev
+        # teacher-forced splice: the oracle takes the GPU's selection, mass and o_prev; the
+        # spliced scores it leaves for the next selection are compared too
         o_tf = np.zeros((B, H, oc.d))
         for b in range(B):
             for h in range(H):
@@ -193,18 +197,33 @@ def check_step(pair: Pair, q, n_dense, k, label=""):
                     m = float(s["mass"][b, h])
                 else:
                     idx, p, m = np.zeros(0, np.int32), np.zeros(0), 0.0
-                o_tf[b, h], _ = orc.attend_sparse(qf, oc.Khat[r][b, h, :n], oc.Vhat[r][b, h, :n],
-                                                  oc.Vhat[r - 1][b, h, :n], idx, p, m,
-                                                  s["o_prev"][b, h].astype(np.float64), float(s["lse_in"][b, h]),
-                                                  s["scores_in"][b, h].astype(np.float64))
+                o_tf[b, h], sc_tf = orc.attend_sparse(qf, oc.Khat[r][b, h, :n], oc.Vhat[r][b, h, :n],
+                                                      oc.Vhat[r - 1][b, h, :n], idx, p, m,
+                                                      s["o_prev"][b, h].astype(np.float64),
+                                                      float(s["lse_in"][b, h]),
+                                                      s["scores_in"][b, h].astype(np.float64))
+                np.testing.assert_allclose(s["scores"][b, h], sc_tf, rtol=0, atol=2e-4,
+                                           err_msg=f"{label} loop {r + 1} spliced scores b={b} h={h}")
         assert_out(s["o"], o_tf, f"{label} loop {r + 1} sparse o (teacher-forced)")
         # end to end against the untaught oracle
         assert_out(s["o"], ref[r]["o"], f"{label} loop {r + 1} sparse o (end-to-end)")
-        if k > 0:
+        if 0 < k < n:
+            # Untaught selections: where the oracle's selection input has a gap of more than
+            # 1e-3 between its k-th and (k+1)-th largest scores (five times the score
+            # tolerance) and every earlier selection of the head matched, the sets must be
+            # identical; elsewhere near-ties may resolve differently, so report the Jaccard.
             jac = []
+            prev = ref[r - 1]["scores"]
             for b in range(B):
                 for h in range(H):
                     a, c = set(s["idx"][b, h].tolist()), set(ref[r]["idx"][b][h].tolist())
                     jac.append(len(a & c) / max(1, len(a | c)))
-            say(f"  {label} loop {r + 1} selection Jaccard vs untaught oracle: min {min(jac):.4f}")
+                    top = np.sort(prev[b, h].astype(np.float32))[::-1]
+                    if same[b, h] and float(top[k - 1]) - float(top[k]) > 1e-3:
+                        gapped += 1
+                        assert a == c, f"{label} loop {r + 1} gapped selection b={b} h={h} differs"
+                    same[b, h] &= a == c
+            say(f"  {label} loop {r + 1} selection Jaccard vs untaught oracle: min {min(jac):.4f}; "
+                f"gapped (b, h) so far asserted identical: {gapped}")
+    pair.gapped = gapped
     return snaps, ref

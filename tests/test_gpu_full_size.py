@@ -58,3 +58,8 @@ def test_batch8_sampled_heads():
     compare_planes(p.gpu, p.orc, [5], [0])
     say("batch8: decode step")
     check_step(p, p.queries(0), w.n_dense, w.k_cols(w.n), "batch8")
+    say("batch8: 64 generated tokens (the last flushes 64 tail rows of every sequence)")
+    for step in range(64):
+        p.append(step)
+    compare_planes(p.gpu, p.orc, [5], [0])
+    check_step(p, p.queries(64), w.n_dense, w.k_cols(p.gpu.n_ctx), "batch8 after 64 steps")

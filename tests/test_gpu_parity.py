@@ -25,6 +25,9 @@ def test_tiny_codes_and_step():
     p = Pair(w, extra=80)
     compare_planes(p.gpu, p.orc, [0], [0])
     check_step(p, p.queries(0), w.n_dense, w.k_cols(p.n), "tiny")
+    # the untaught selections of both sparse loops sit on gapped scores here, and are
+    # asserted identical to the oracle's
+    assert p.gapped == 2
 
 
 def test_tiny_decode_with_flush():

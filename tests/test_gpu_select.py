@@ -80,3 +80,18 @@ def test_few_ties_at_and_near_the_threshold(n, k):
     say(f"  select few ties n={n} k={k}")
     for kk in (k - 1, k, k + 1):
         run_case(S, lse, kk)
+
+
+@pytest.mark.parametrize("n", [4097, 32769])
+def test_offset_rows(n):
+    # scores far from zero relative to their spread (|min| / (max - min) from 1e3 to 1e6): a
+    # bin formula with a rounded bias would put the smallest scores below the first bin
+    g = np.random.default_rng(n + 99)
+    S = np.zeros((1, 4, n), np.float32)
+    for h, (off, spread) in enumerate(((1000.0, 0.05), (-2000.0, 0.01), (50.0, 1e-4), (3e4, 0.02))):
+        S[0, h] = (off + spread * g.standard_normal(n)).astype(np.float32)
+    lse = np.log(np.exp((S - S.max(-1, keepdims=True)).astype(np.float64)).sum(-1)).astype(np.float32)
+    lse = (lse + S.max(-1)).astype(np.float32)
+    for k in (1, -(-n // 10), n - 1):
+        say(f"  select offset rows n={n} k={k}")
+        run_case(S, lse, k)
