@@ -41,6 +41,7 @@ extern "C" {
 #endif
 
 #define QKV_MAX_LOOPS 32
+#define QKV_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)  /* attn_decode_dense_noalloc's fixed scratch */
 #define QKV_GROUP 64
 #define QKV_TAIL_SLOTS 128
 
@@ -174,6 +175,23 @@ int kv_append_tail(const qkv_cache* cache, int loop, int pos0, int n_rows,
 int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,
                       const uint16_t* v_new, float sm_scale, uint16_t* o, float* o_f32, float* scores,
                       int ld_scores, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * attn_decode_dense_noalloc - attn_decode_dense without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, outputs and kernels as
+ * attn_decode_dense; the split partials go to a fixed device array inside the library,
+ * QKV_NOALLOC_SCRATCH_BYTES (4 MiB) per GPU, held from the first call on a GPU until the
+ * process ends.  The call allocates nothing.
+ *   Returns QKV_EWORKSPACE (nothing queued) when the partials of this shape, i.e. the
+ *   workspace attn_decode_dense would need for the current n_ctx, exceed that size (about
+ *   8000 (split, sequence, head) partials at head_dim 128).
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ *   race (the array needs no clearing: each call writes every partial it reads).
+ */
+int attn_decode_dense_noalloc(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,
+                              const uint16_t* v_new, float sm_scale, uint16_t* o, float* o_f32, float* scores,
+                              int ld_scores, float* lse, void* stream);
 
 /*
  * select_columns - top-k columns of each (sequence, head) under the distribution

@@ -20,7 +20,9 @@ TAIL_SLOTS = 128
 QKV_OK, QKV_EINVAL, QKV_EUNSUPPORTED, QKV_ECAPACITY, QKV_ELAUNCH, QKV_EWORKSPACE = 0, -1, -2, -3, -4, -5
 
 EXPORTED = ("qkv_strerror", "qkv_block_bytes", "qkv_body_len", "qkv_workspace_bytes", "kv_encode_loop",
-            "kv_append_tail", "attn_decode_dense", "select_columns", "attn_decode_sparse", "qkv_stream_read")
+            "kv_append_tail", "attn_decode_dense", "attn_decode_dense_noalloc", "select_columns",
+            "attn_decode_sparse", "qkv_stream_read")
+NOALLOC_SCRATCH_BYTES = 4 << 20
 STREAM_READ_GROUPS = 2048
 
 
@@ -69,6 +71,8 @@ def lib():
     L.kv_append_tail.restype = i32
     L.attn_decode_dense.argtypes = [cp, i32, vp, vp, vp, f32, vp, vp, vp, i32, vp, vp, sz, vp]
     L.attn_decode_dense.restype = i32
+    L.attn_decode_dense_noalloc.argtypes = [cp, i32, vp, vp, vp, f32, vp, vp, vp, i32, vp, vp]
+    L.attn_decode_dense_noalloc.restype = i32
     L.select_columns.argtypes = [vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.select_columns.restype = i32
     L.qkv_stream_read.argtypes = [vp, sz, vp, vp]
@@ -141,6 +145,15 @@ def attn_decode_dense(cache, loop, q, sm_scale, o, o_f32, scores, lse, ws, strea
                                  ws.numel() * ws.element_size(),
                                  _stream(stream))
     _check("attn_decode_dense", st)
+
+
+def attn_decode_dense_noalloc(cache, loop, q, sm_scale, o, o_f32, scores, lse, stream=None, k_new=None, v_new=None):
+    """attn_decode_dense with the split partials in the library's fixed device scratch
+    (NOALLOC_SCRATCH_BYTES per GPU) instead of a workspace: allocates nothing."""
+    st = lib().attn_decode_dense_noalloc(ctypes.byref(cache.desc), loop, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                         float(sm_scale), _ptr(o), _ptr(o_f32), _ptr(scores),
+                                         0 if scores is None else scores.shape[-1], _ptr(lse), _stream(stream))
+    _check("attn_decode_dense_noalloc", st)
 
 
 def select_columns(scores, lse, n, k, idx, p_sel, mass, ws=None, stream=None):

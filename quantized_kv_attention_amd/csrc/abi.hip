@@ -157,6 +157,22 @@ int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, const
                         lse, ws, to_stream(stream));
 }
 
+int attn_decode_dense_noalloc(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,
+                              const uint16_t* v_new, float sm_scale, uint16_t* o, float* o_f32, float* scores,
+                              int ld_scores, float* lse, void* stream) {
+    CacheArg a;
+    int st = make_arg(cache, &a);
+    if (st) return st;
+    if (loop < 1 || loop > cache->n_loops) return QKV_EINVAL;
+    if (cache->n_ctx < 1) return QKV_EINVAL;
+    if (!q || !o_f32 || !lse || (scores && ld_scores < cache->n_ctx)) return QKV_EINVAL;
+    if (!aligned16(q) || !aligned16(o_f32) || (o && !aligned16(o))) return QKV_EINVAL;
+    if ((k_new == nullptr) != (v_new == nullptr) || (k_new && (!aligned16(k_new) || !aligned16(v_new))))
+        return QKV_EINVAL;
+    return launch_dense_noalloc(a, cache->head_dim, loop, q, NewRow{k_new, v_new}, sm_scale, o, o_f32, scores,
+                                ld_scores, lse, to_stream(stream));
+}
+
 int select_columns(const float* scores, int ld_scores, const float* lse, int batch, int heads, int n, int k,
                    int32_t* idx, float* p_sel, float* mass, void* ws, size_t ws_bytes, void* stream) {
     if (!scores || !lse || !mass || batch < 1 || heads < 1 || n < 1 || ld_scores < n) return QKV_EINVAL;

@@ -29,6 +29,9 @@ size_t dense_ws_bytes(int B, int H, int D, int n_body);
 int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, uint16_t* o, float* o32,
                  float* scores, int ld, float* lse, void* ws, hipStream_t st);
 
+int launch_dense_noalloc(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, uint16_t* o,
+                         float* o32, float* scores, int ld, float* lse, hipStream_t st);
+
 size_t select_ws_bytes(int B, int H, int n);
 int launch_select(const float* scores, int ld, const float* lse, int B, int H, int n, int k, int32_t* idx,
                   float* p_sel, float* mass, void* ws, hipStream_t st);
