@@ -48,11 +48,13 @@ def lib():
         f64p = ctypes.POINTER(ctypes.c_double)
         u8p = ctypes.POINTER(ctypes.c_uint8)
         i32p = ctypes.POINTER(ctypes.c_int32)
-        L.orc_quantize_group.argtypes = [f32p, ctypes.c_int, ctypes.c_long, u8p, ctypes.c_long, f32p, f32p]
+        L.orc_quantize_group.argtypes = [f32p, ctypes.c_int, ctypes.c_long, ctypes.c_int, u8p, ctypes.c_long, f32p,
+                                         f32p]
         L.orc_quantize_group.restype = None
         L.orc_dequant.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float]
         L.orc_dequant.restype = ctypes.c_float
-        L.orc_encode_rows.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, f32p, f32p, u8p, f32p, f32p, f32p]
+        L.orc_encode_rows.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, f32p, f32p, u8p, f32p,
+                                      f32p, f32p]
         L.orc_encode_rows.restype = None
         L.orc_attend_dense.argtypes = [ctypes.c_int, ctypes.c_int, f32p, ctypes.c_double, f32p, f32p, f64p, f64p, f64p]
         L.orc_attend_dense.restype = None
@@ -83,15 +85,16 @@ def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------
-# Codec (explainer section 3: asymmetric INT4, group 64)
+# Codec (explainer section 3: asymmetric INT4, group 64; 2-bit codes for the residual
+# precision setting of the project page's "Main Results" sweep)
 # ----------------------------------------------------------------------------------
-def quantize_group(x: np.ndarray):
+def quantize_group(x: np.ndarray, bits: int = 4):
     x = np.ascontiguousarray(x, dtype=np.float32)
     m = x.shape[0]
     codes = np.zeros(m, np.uint8)
     s = np.zeros(1, np.float32)
     z = np.zeros(1, np.float32)
-    lib().orc_quantize_group(_p(x, ctypes.c_float), m, 1, _p(codes, ctypes.c_uint8), 1,
+    lib().orc_quantize_group(_p(x, ctypes.c_float), m, 1, int(bits), _p(codes, ctypes.c_uint8), 1,
                              _p(s, ctypes.c_float), _p(z, ctypes.c_float))
     return codes, s[0], z[0]
 
@@ -105,8 +108,9 @@ def dequant(codes: np.ndarray, s, z) -> np.ndarray:
     return out
 
 
-def encode_rows(X: np.ndarray, P, is_key: bool):
-    """Encode one call's stored rows (ascending positions) of one (sequence, head).
+def encode_rows(X: np.ndarray, P, is_key: bool, bits: int = 4):
+    """Encode one call's stored rows (ascending positions) of one (sequence, head):
+    X - P quantized with `bits`-bit codes (P None: X itself).
 
     Returns codes [nrows,d] u8, s, z (keys: [ceil(nrows/64), d]; values: [nrows, d/64])
     and the new reconstruction R [nrows, d] f32.
@@ -128,7 +132,7 @@ def encode_rows(X: np.ndarray, P, is_key: bool):
     if P is not None:
         P = np.ascontiguousarray(P, dtype=np.float32)
         Pp = _p(P, ctypes.c_float)
-    lib().orc_encode_rows(nrows, d, 1 if is_key else 0, _p(X, ctypes.c_float), Pp,
+    lib().orc_encode_rows(nrows, d, 1 if is_key else 0, int(bits), _p(X, ctypes.c_float), Pp,
                           _p(codes, ctypes.c_uint8), _p(s, ctypes.c_float), _p(z, ctypes.c_float),
                           _p(R, ctypes.c_float))
     return codes, s, z, R
@@ -233,9 +237,20 @@ class OracleCache:
     Khat[r], Vhat[r] hold the loop-(r+1) reconstruction of every cached position
     (float32 [B, H, cap, d]): quantized chain for body positions, exact BF16 values in
     the tail.  act[r] is the loop's active-token mask per sequence ([B, cap] bool).
+
+    Codec variants (the project page's "Main Results" precision sweep; the explainer's
+    sections 4 and 5):
+      residual_bits  bits of the residual planes of loops >= 2 (4, or 2); loop 1's base
+                     is always 4-bit;
+      full_state     True: every loop stores its own K/V quantized with 4-bit codes, not a
+                     residual (the "Per-loop KIVI4" ablation row); an inactive row still
+                     keeps the previous loop's reconstruction.
     """
 
-    def __init__(self, B: int, H: int, d: int, R: int, cap: int):
+    def __init__(self, B: int, H: int, d: int, R: int, cap: int, residual_bits: int = 4,
+                 full_state: bool = False):
+        assert residual_bits in (2, 4) and not (full_state and residual_bits != 4)
+        self.residual_bits, self.full_state = residual_bits, full_state
         self.B, self.H, self.d, self.R, self.cap = B, H, d, R, cap
         self.n = 0
         self.nb = 0
@@ -255,8 +270,9 @@ class OracleCache:
                     out = {}
                     for name, Xin, Xhat in (("k", self.Kin, self.Khat), ("v", self.Vin, self.Vhat)):
                         X = Xin[r][b, h, rows]
-                        P = None if r == 0 else Xhat[r - 1][b, h, rows]
-                        codes, s, z, Rc = encode_rows(X, P, is_key=(name == "k"))
+                        P = None if (r == 0 or self.full_state) else Xhat[r - 1][b, h, rows]
+                        bits = 4 if (r == 0 or self.full_state) else self.residual_bits
+                        codes, s, z, Rc = encode_rows(X, P, is_key=(name == "k"), bits=bits)
                         out[name] = (codes, s, z)
                         # active rows: new reconstruction; inactive rows keep loop r-1's
                         if r > 0:

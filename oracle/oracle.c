@@ -39,15 +39,17 @@
 #include <string.h>
 
 #define ORC_GROUP 64
-#define ORC_LEVELS 15.0f
 
 /* ---------------------------------------------------------------------------------
  * Quantizer [P5 section 3]: asymmetric min/max over one group of m <= 64 values
- * x[0], x[stride], ... .  Writes m codes (one per byte) and the group's fp32 s, z.
+ * x[0], x[stride], ... with 2^bits levels (bits = 4 for the pages' INT4 codec; 2 for
+ * the 2-bit residual setting of the project page's precision sweep, "Main Results", and
+ * of the explainer's section 5).  Writes m codes (one per byte) and the group's fp32 s, z.
  * ------------------------------------------------------------------------------- */
-void orc_quantize_group(const float* x, int m, long stride,
+void orc_quantize_group(const float* x, int m, long stride, int bits,
                         uint8_t* code, long code_stride, float* s_out, float* z_out)
 {
+    const float top = (float)((1 << bits) - 1);  /* largest code: 15 or 3 */
     float mn = x[0], mx = x[0];
     for (int i = 1; i < m; ++i) {
         float v = x[(long)i * stride];
@@ -55,7 +57,7 @@ void orc_quantize_group(const float* x, int m, long stride,
         if (v > mx) mx = v;
     }
     float range = mx - mn;          /* one fp32 subtraction */
-    float s = range / ORC_LEVELS;   /* one fp32 division    */
+    float s = range / top;          /* one fp32 division    */
     s = s + 0.0f;                   /* -0 -> +0             */
     float z = mn + 0.0f;            /* -0 -> +0             */
     for (int i = 0; i < m; ++i) {
@@ -65,7 +67,7 @@ void orc_quantize_group(const float* x, int m, long stride,
             float u = t / s;                    /* fp32 division    */
             float r = rintf(u);                 /* half to even     */
             if (r < 0.0f) r = 0.0f;
-            if (r > 15.0f) r = 15.0f;
+            if (r > top) r = top;
             c = (uint8_t)r;
         }
         code[(long)i * code_stride] = c;
@@ -86,10 +88,13 @@ float orc_dequant(uint8_t c, float s, float z) { return fmaf((float)c, s, z); }
  *                      -> s[ngroups][d], z[ngroups][d]
  *   values (is_key=0): per row over each run of 64 consecutive channels
  *                      -> s[nrows][d/64], z[nrows][d/64]
- * code[nrows][d] one code per byte.  R[nrows][d] receives the new reconstruction
- * (loop 1: dequantised value; later loops: P + dequantised residual, fp32 add).
+ * code[nrows][d] one code per byte, `bits` bits each.  R[nrows][d] receives the new
+ * reconstruction (loop 1: dequantised value; later loops: P + dequantised residual,
+ * fp32 add).  With P == NULL the rows' own values are quantized, which is also how the
+ * per-loop full-state INT4 ablation (explainer section 4, "Per-loop KIVI4") stores
+ * every loop.
  * ------------------------------------------------------------------------------- */
-void orc_encode_rows(int nrows, int d, int is_key, const float* X, const float* P,
+void orc_encode_rows(int nrows, int d, int is_key, int bits, const float* X, const float* P,
                      uint8_t* code, float* s, float* z, float* R)
 {
     float* D = (float*)malloc(sizeof(float) * (size_t)(nrows > 0 ? nrows : 1) * d);
@@ -102,7 +107,7 @@ void orc_encode_rows(int nrows, int d, int is_key, const float* X, const float* 
             int r0 = g * ORC_GROUP;
             int m = nrows - r0 < ORC_GROUP ? nrows - r0 : ORC_GROUP;
             for (int c = 0; c < d; ++c)
-                orc_quantize_group(D + (long)r0 * d + c, m, d,
+                orc_quantize_group(D + (long)r0 * d + c, m, d, bits,
                                    code + (long)r0 * d + c, d,
                                    s + (long)g * d + c, z + (long)g * d + c);
         }
@@ -116,7 +121,7 @@ void orc_encode_rows(int nrows, int d, int is_key, const float* X, const float* 
         int gpr = d / ORC_GROUP;
         for (int i = 0; i < nrows; ++i)
             for (int g = 0; g < gpr; ++g)
-                orc_quantize_group(D + (long)i * d + g * ORC_GROUP, ORC_GROUP, 1,
+                orc_quantize_group(D + (long)i * d + g * ORC_GROUP, ORC_GROUP, 1, bits,
                                    code + (long)i * d + g * ORC_GROUP, 1,
                                    s + (long)i * gpr + g, z + (long)i * gpr + g);
         for (int i = 0; i < nrows; ++i)
