@@ -56,16 +56,19 @@ enum {
 
 /*
  * One loop's stored plane (loop p = index + 1).  Layout of `data`, device memory:
- *   [batch][heads][n_blocks][block], one block = 64 consecutive storage slots, with
- *   d = 128: block = K codes [64][64] | V records [64] of (V codes [64] | (s, z) [2], fp32)
- *                    | K s[128], K z[128] (fp32)                    -> 10240 bytes
- *   d = 64:  block = K codes [64][32] | V codes [64][32] | K s[64], K z[64] (fp32)
- *                    | V meta [64] of (s, z) (fp32)                 -> 5120 bytes
- *   (at d = 128 a slot's value codes and value meta are adjacent, 80 bytes per slot, so a
- *   gather of one slot's value touches fewer 128-byte lines).
- *   A code byte holds channel 2i in its low nibble and channel 2i+1 in its high nibble.
+ *   [batch][heads][n_blocks][block], one block = 64 consecutive storage slots.  With
+ *   c = head_dim * bits / 8 code bytes per slot (bits: see qkv_cache.residual_bits):
+ *   d = 128: block = K codes [64][c] | V records [64] of (V codes [c] | (s, z) [2], fp32)
+ *                    | K s[128], K z[128] (fp32)       -> 10240 bytes (4-bit), 6144 (2-bit)
+ *   d = 64:  block = K codes [64][c] | V codes [64][c] | K s[64], K z[64] (fp32)
+ *                    | V meta [64] of (s, z) (fp32)    -> 5120 bytes (4-bit), 3072 (2-bit)
+ *   (at d = 128 a slot's value codes and value meta are adjacent, so a gather of one
+ *   slot's value touches fewer 128-byte lines).
+ *   4-bit codes: a byte holds channel 2i in its low nibble and channel 2i+1 in its high
+ *   nibble.  2-bit codes: byte i holds channels 4i..4i+3, channel 4i+m in bits 2m, 2m+1.
  *   Key group = one block (64 consecutive slots) per channel; value group = one slot
- *   over 64 consecutive channels.  Dequantised value = fmaf(code, s, z).
+ *   over 64 consecutive channels.  Dequantised value = fmaf(code, s, z), with
+ *   s = (max - min) / (2^bits - 1).
  * A dense plane stores every body position at slot == position.  A sparse plane stores
  * the active positions in ascending order; each encode call starts on a new block and
  * pads its last block (padding slots: codes 0, value meta 0, rowpos -1).  Sparse planes
@@ -108,13 +111,25 @@ typedef struct qkv_cache {
      * (kv_encode_loop maintains it).  With it, a gather over a deep chain reads only the
      * planes that store a column; without it, it looks the column up in every plane. */
     uint32_t* stored_loops;
+    /* Codec [project page, "Main Results": precision sweep of the KV residual quantization;
+     * explainer sections 4 and 5: the "Per-loop KIVI4" ablation and the 2-bit setting]:
+     *   residual_bits  code width of the planes of loops >= 2: 4 (or 0, read as 4) or 2;
+     *                  loop 1's base is always 4-bit;
+     *   full_state     0: loop r >= 2 stores the residual X^(r) - Xhat^(r-1) (the chain is
+     *                  the sum of the stored planes); 1: every loop stores its own X^(r)
+     *                  with 4-bit codes, and a position's K/V in loop r is that of the last
+     *                  loop <= r that stores it (requires residual_bits 4). */
+    int32_t residual_bits;
+    int32_t full_state;
 } qkv_cache;
 
 /* Human-readable text of a status code (static storage). */
 const char* qkv_strerror(int status);
 
-/* Bytes of one 64-slot block for head_dim d (d = 128: 10240; d = 64: 5120), 0 if unsupported. */
-size_t qkv_block_bytes(int head_dim);
+/* Bytes of one 64-slot block for head_dim d and `bits`-bit codes (see qkv_plane), 0 if
+ * unsupported.  A plane's blocks are 4-bit for loop 1 and for the full-state codec,
+ * residual_bits otherwise. */
+size_t qkv_block_bytes(int head_dim, int bits);
 
 /* Body length for a context of n positions (see qkv_cache). */
 int qkv_body_len(int n_ctx);
@@ -230,6 +245,20 @@ int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, cons
                        const int32_t* idx, const float* p_sel, const float* mass, int k,
                        const float* o_prev, const float* lse, float* scores, int ld_scores,
                        uint16_t* o, float* o_f32, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qkv_export_plane - unpacks slots [0, n_slots) of loop `loop`'s plane for sequence b, head
+ * h into plain arrays, so that a test can compare a plane's logical content with a
+ * reference without decoding the packed layout above (test and inspection use; not on
+ * the decode path).  All outputs are device memory owned by the caller:
+ *   k_codes, v_codes  uint8 [n_slots][head_dim], one code per byte;
+ *   k_scale, k_zero   fp32 [ceil(n_slots / 64)][head_dim] (one key group per block);
+ *   v_scale, v_zero   fp32 [n_slots][head_dim / 64].
+ * 1 <= n_slots <= the plane's n_blocks * 64.  Asynchronous on `stream`.
+ */
+int qkv_export_plane(const qkv_cache* cache, int loop, int b, int h, int n_slots, uint8_t* k_codes,
+                     uint8_t* v_codes, float* k_scale, float* k_zero, float* v_scale, float* v_zero,
+                     void* stream);
 
 /*
  * qkv_stream_read - bandwidth reference, not part of the attention path: reads n_bytes from

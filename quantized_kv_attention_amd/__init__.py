@@ -21,7 +21,7 @@ QKV_OK, QKV_EINVAL, QKV_EUNSUPPORTED, QKV_ECAPACITY, QKV_ELAUNCH, QKV_EWORKSPACE
 
 EXPORTED = ("qkv_strerror", "qkv_block_bytes", "qkv_body_len", "qkv_workspace_bytes", "kv_encode_loop",
             "kv_append_tail", "attn_decode_dense", "attn_decode_dense_noalloc", "select_columns",
-            "attn_decode_sparse", "qkv_stream_read")
+            "attn_decode_sparse", "qkv_export_plane", "qkv_stream_read")
 NOALLOC_SCRATCH_BYTES = 4 << 20
 STREAM_READ_GROUPS = 2048
 
@@ -41,7 +41,8 @@ class QkvCache(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("n_loops", ctypes.c_int32), ("cap_ctx", ctypes.c_int32), ("n_ctx", ctypes.c_int32),
                 ("plane", QkvPlane * MAX_LOOPS), ("tail_k", ctypes.c_void_p * MAX_LOOPS),
-                ("tail_v", ctypes.c_void_p * MAX_LOOPS), ("stored_loops", ctypes.c_void_p)]
+                ("tail_v", ctypes.c_void_p * MAX_LOOPS), ("stored_loops", ctypes.c_void_p),
+                ("residual_bits", ctypes.c_int32), ("full_state", ctypes.c_int32)]
 
 
 _lib = None
@@ -59,7 +60,7 @@ def lib():
     cp = ctypes.POINTER(QkvCache)
     L.qkv_strerror.argtypes = [i32]
     L.qkv_strerror.restype = ctypes.c_char_p
-    L.qkv_block_bytes.argtypes = [i32]
+    L.qkv_block_bytes.argtypes = [i32, i32]
     L.qkv_block_bytes.restype = sz
     L.qkv_body_len.argtypes = [i32]
     L.qkv_body_len.restype = i32
@@ -75,6 +76,8 @@ def lib():
     L.attn_decode_dense_noalloc.restype = i32
     L.select_columns.argtypes = [vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.select_columns.restype = i32
+    L.qkv_export_plane.argtypes = [cp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.qkv_export_plane.restype = i32
     L.qkv_stream_read.argtypes = [vp, sz, vp, vp]
     L.qkv_stream_read.restype = i32
     L.attn_decode_sparse.argtypes = [cp, i32, vp, vp, vp, f32, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, sz, vp]
@@ -87,8 +90,8 @@ def strerror(status: int) -> str:
     return lib().qkv_strerror(int(status)).decode()
 
 
-def block_bytes(head_dim: int) -> int:
-    return int(lib().qkv_block_bytes(head_dim))
+def block_bytes(head_dim: int, bits: int = 4) -> int:
+    return int(lib().qkv_block_bytes(head_dim, bits))
 
 
 def body_len(n_ctx: int) -> int:
@@ -174,6 +177,25 @@ def attn_decode_sparse(cache, loop, q, sm_scale, idx, p_sel, mass, k, o_prev, ls
                                   0 if scores is None else scores.shape[-1], _ptr(o),
                                   _ptr(o_f32), _ptr(ws), wsb, _stream(stream))
     _check("attn_decode_sparse", st)
+
+
+def export_plane(cache, loop, b, h, n_slots, stream=None):
+    """Slots [0, n_slots) of loop `loop`'s plane for (b, h), unpacked by the library:
+    dict of device tensors kc, vc (uint8 [n_slots, d]), ks, kz (fp32 [ceil(n_slots/64), d]),
+    vs, vz (fp32 [n_slots, d/64])."""
+    import torch
+    d = cache.d
+    dev = cache.planes[loop - 1].device
+    out = dict(kc=torch.empty((n_slots, d), dtype=torch.uint8, device=dev),
+               vc=torch.empty((n_slots, d), dtype=torch.uint8, device=dev),
+               ks=torch.empty(((n_slots + 63) // 64, d), dtype=torch.float32, device=dev),
+               kz=torch.empty(((n_slots + 63) // 64, d), dtype=torch.float32, device=dev),
+               vs=torch.empty((n_slots, d // 64), dtype=torch.float32, device=dev),
+               vz=torch.empty((n_slots, d // 64), dtype=torch.float32, device=dev))
+    st = lib().qkv_export_plane(ctypes.byref(cache.desc), loop, b, h, n_slots, _ptr(out["kc"]), _ptr(out["vc"]),
+                                _ptr(out["ks"]), _ptr(out["kz"]), _ptr(out["vs"]), _ptr(out["vz"]), _stream(stream))
+    _check("qkv_export_plane", st)
+    return out
 
 
 from .cache import LayerCache, DecodeBuffers  # noqa: E402

@@ -23,25 +23,32 @@ class LayerCache:
     dense[r]: loop r+1 stores every body position (loop 1 must be dense).
     sparse_blocks[r]: capacity in 64-slot blocks of a sparse plane (default: enough
     for every position).
+    residual_bits: code width of the planes of loops >= 2 (4 or 2; the base is 4-bit).
+    full_state: every loop stores its own K/V with 4-bit codes instead of a residual.
     """
 
     def __init__(self, batch, heads, head_dim, n_loops, cap_ctx, dense=None, sparse_blocks=None,
-                 device="cuda"):
+                 device="cuda", residual_bits=4, full_state=False):
         assert n_loops <= MAX_LOOPS and cap_ctx % GROUP == 0
+        assert residual_bits in (2, 4) and not (full_state and residual_bits != 4)
         self.B, self.H, self.d, self.R, self.cap = batch, heads, head_dim, n_loops, cap_ctx
         self.device = device
+        self.residual_bits, self.full_state = residual_bits, bool(full_state)
         dense = [True, True] + [False] * (n_loops - 2) if dense is None else list(dense)
         dense = (dense + [dense[-1]] * n_loops)[:n_loops]
         assert dense[0], "loop 1 (the base) stores every position"
         self.dense = dense
-        bb = block_bytes(head_dim)
-        self.block_bytes = bb
+        self.bits = [4 if (r == 0 or full_state) else residual_bits for r in range(n_loops)]
+        self.block_bytes_of = [block_bytes(head_dim, b) for b in self.bits]
+        self.block_bytes = self.block_bytes_of[0]
         self.planes, self.rowmap, self.rowpos, self.rowstart = [], [], [], []
         self.tail_k, self.tail_v = [], []
         desc = QkvCache()
         desc.batch, desc.heads, desc.head_dim, desc.n_loops = batch, heads, head_dim, n_loops
         desc.cap_ctx, desc.n_ctx = cap_ctx, 0
+        desc.residual_bits, desc.full_state = residual_bits, 1 if full_state else 0
         for r in range(n_loops):
+            bb = self.block_bytes_of[r]
             nblk = cap_ctx // GROUP
             if not dense[r] and sparse_blocks is not None:
                 nblk = int(sparse_blocks[r])

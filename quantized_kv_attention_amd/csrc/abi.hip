@@ -24,6 +24,12 @@ int make_arg(const qkv_cache* c, CacheArg* a) {
     a->n_ctx = c->n_ctx;
     a->n_body = body_len(c->n_ctx);
     a->nplanes = c->n_loops;
+    const int rb = c->residual_bits == 0 ? 4 : c->residual_bits;
+    if (rb != 4 && rb != 2) return QKV_EUNSUPPORTED;
+    if (c->full_state != 0 && c->full_state != 1) return QKV_EINVAL;
+    if (c->full_state && rb != 4) return QKV_EUNSUPPORTED;  // the full-state codec is 4-bit
+    a->rbits = rb;
+    a->full = c->full_state;
     if (c->stored_loops && !aligned16(c->stored_loops)) return QKV_EINVAL;
     a->smask = c->stored_loops;
     for (int p = 0; p < QKV_MAX_LOOPS; ++p) {
@@ -72,9 +78,11 @@ const char* qkv_strerror(int status) {
     }
 }
 
-size_t qkv_block_bytes(int head_dim) {
-    if (head_dim == 128) return Block<128>::kBytes;
-    if (head_dim == 64) return Block<64>::kBytes;
+size_t qkv_block_bytes(int head_dim, int bits) {
+    if (bits == 4 && head_dim == 128) return Block<128, 4>::kBytes;
+    if (bits == 4 && head_dim == 64) return Block<64, 4>::kBytes;
+    if (bits == 2 && head_dim == 128) return Block<128, 2>::kBytes;
+    if (bits == 2 && head_dim == 64) return Block<64, 2>::kBytes;
     return 0;
 }
 
@@ -201,6 +209,19 @@ int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, cons
     if (k > 0 && (!ws || ws_bytes < need)) return QKV_EWORKSPACE;
     return launch_sparse(a, cache->head_dim, loop, q, NewRow{k_new, v_new}, sm_scale, idx, p_sel, mass, k, o_prev,
                          lse, scores, ld_scores, o, o_f32, ws, to_stream(stream));
+}
+
+int qkv_export_plane(const qkv_cache* cache, int loop, int b, int h, int n_slots, uint8_t* k_codes,
+                     uint8_t* v_codes, float* k_scale, float* k_zero, float* v_scale, float* v_zero, void* stream) {
+    CacheArg a;
+    int st = make_arg(cache, &a);
+    if (st) return st;
+    if (loop < 1 || loop > cache->n_loops || b < 0 || b >= cache->batch || h < 0 || h >= cache->heads)
+        return QKV_EINVAL;
+    if (n_slots < 1 || (long)n_slots > (long)cache->plane[loop - 1].n_blocks * 64) return QKV_EINVAL;
+    if (!k_codes || !v_codes || !k_scale || !k_zero || !v_scale || !v_zero) return QKV_EINVAL;
+    return launch_export_plane(a, cache->head_dim, loop, b, h, n_slots, k_codes, v_codes, k_scale, k_zero, v_scale,
+                               v_zero, to_stream(stream));
 }
 
 int qkv_stream_read(const void* src, size_t n_bytes, uint32_t* sink, void* stream) {

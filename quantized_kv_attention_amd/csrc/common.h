@@ -12,32 +12,41 @@ constexpr int kGroup = QKV_GROUP;        // tokens per key group / channels per 
 constexpr int kTail = QKV_TAIL_SLOTS;    // BF16 tail ring slots
 constexpr int kWave = 64;
 
-// One 64-slot block of a plane, head dimension D (bytes).
-template <int D>
+// One 64-slot block of a plane, head dimension D, BITS-bit codes (4, or 2 for 2-bit
+// residual planes).  Offsets in bytes.
+template <int D, int BITS = 4>
 struct Block {
-    static constexpr int kRowBytes = D / 2;             // packed codes of one slot
+    static_assert(BITS == 4 || BITS == 2, "4- or 2-bit codes");
+    static constexpr int kRowBytes = D * BITS / 8;      // packed codes of one slot
     static constexpr int kVGroups = D / 64;
-    // d = 128: K codes [64][64] | V records [64][64 code bytes + 2 x (s, z)] | K s[D], z[D].
-    // A slot's value codes and value meta sit together (80 bytes), so a gathered slot's
-    // value takes 1.5 lines of 128 bytes on average instead of 2.
-    // d = 64: K codes [64][32] | V codes [64][32] | K s[D], z[D] | V meta [64] x (s, z)
-    // (a 40-byte record would break the 16-byte alignment of the code loads).
+    // d = 128: K codes [64][kRowBytes] | V records [64][kRowBytes code bytes + 2 x (s, z)]
+    //          | K s[D], z[D].  A slot's value codes and value meta sit together (80 bytes
+    //          at 4 bits), so a gathered slot's value takes fewer 128-byte lines.
+    // d = 64:  K codes [64][kRowBytes] | V codes [64][kRowBytes] | K s[D], z[D]
+    //          | V meta [64] x (s, z) (a 40-byte record would break the 16-byte alignment
+    //          of the code loads).
     static constexpr bool kVRec = (D == 128);
-    static constexpr int kKc = 0;                                            // K codes [64][D/2]
-    static constexpr int kV = 64 * D / 2;                                    // value region
-    static constexpr int kVStride = kVRec ? D / 2 + kVGroups * 8 : D / 2;    // value codes: bytes per slot
-    static constexpr int kKm = kVRec ? kV + 64 * kVStride : 64 * D;         // K s[D], z[D]
-    static constexpr int kVmArr = 64 * D + D * 8;                            // d = 64: V meta array
+    static constexpr int kKc = 0;                                            // K codes
+    static constexpr int kV = 64 * kRowBytes;                                // value region
+    static constexpr int kVStride = kVRec ? kRowBytes + kVGroups * 8 : kRowBytes;
+    static constexpr int kKm = kVRec ? kV + 64 * kVStride : 2 * 64 * kRowBytes;  // K s[D], z[D]
+    static constexpr int kVmArr = 2 * 64 * kRowBytes + D * 8;                // d = 64: V meta array
     static constexpr int kBytes = kVRec ? kKm + D * 8 : kVmArr + 64 * kVGroups * 8;
-    // offsets of slot `row`'s value codes and of its value meta (s, z) for group 0
+    // offsets of slot `row`'s key codes, value codes and value meta (s, z) for group 0
+    __host__ __device__ static constexpr int kc(int row) { return kKc + row * kRowBytes; }
     __host__ __device__ static constexpr int vc(int row) { return kV + row * kVStride; }
     __host__ __device__ static constexpr int vm(int row) {
-        return kVRec ? kV + row * kVStride + D / 2 : kVmArr + row * kVGroups * 8;
+        return kVRec ? kV + row * kVStride + kRowBytes : kVmArr + row * kVGroups * 8;
     }
-    // lanes per row when each lane owns 32 channels (16 code bytes)
+    // lanes per row when each lane owns 32 channels (16 code bytes at 4 bits, 8 at 2)
     static constexpr int kLpr = D / 32;
     static constexpr int kRpi = kWave / kLpr;           // rows covered by one wave load
+    static constexpr int kLaneBytes = 32 * BITS / 8;    // code bytes of a lane's 32 channels
 };
+
+// Code width of plane p (0-based) of a cache: the base is 4-bit; residual planes carry RB
+// bits; in the full-state codec every plane is 4-bit.
+__host__ __device__ constexpr int plane_bits(int p, int RB, bool FULL) { return (p == 0 || FULL) ? 4 : RB; }
 
 // Per-plane view passed by value in kernel arguments.
 struct PlaneArg {
@@ -52,6 +61,8 @@ struct PlaneArg {
 struct CacheArg {
     int32_t B, H, cap_ctx, n_ctx, n_body;
     int32_t nplanes;
+    int32_t rbits;     // code width of residual planes (4 or 2)
+    int32_t full;      // 1: full-state codec (every loop stores its own K/V)
     PlaneArg p[QKV_MAX_LOOPS];
     const uint16_t* tail_k[QKV_MAX_LOOPS];
     const uint16_t* tail_v[QKV_MAX_LOOPS];
@@ -66,9 +77,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-template <int D>
+template <int D, int BITS = 4>
 __device__ __forceinline__ const uint8_t* block_ptr(const PlaneArg& P, int H, int b, int h, int blk) {
-    return P.data + ((size_t)((size_t)b * H + h) * P.n_blocks + blk) * Block<D>::kBytes;
+    return P.data + ((size_t)((size_t)b * H + h) * P.n_blocks + blk) * Block<D, BITS>::kBytes;
 }
 
 // Orders one wave's LDS writes before its later LDS reads by other lanes of the same wave.
@@ -303,6 +314,61 @@ __device__ __forceinline__ void axpy32_fp8(const uint4 w, float wt, float* acc) 
     }
 }
 
+// ---- 2-bit codes (channel 4i + m in bits 2m, 2m + 1 of byte i) through the FP8 converter:
+// a byte b in [0, 3] read as E4M3 is the subnormal b * 2^-9, as for the 4-bit codes ----
+// 16 codes of one 32-bit word, times 2^-9, in channel order
+__device__ __forceinline__ void codes16_fp8_2b(uint32_t w, float* c) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t x = (w >> (2 * m)) & 0x03030303u;   // channels m, 4 + m, 8 + m, 12 + m
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
+        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
+        c[m] = a.x; c[4 + m] = a.y; c[8 + m] = b.x; c[12 + m] = b.y;
+    }
+}
+
+// sum_c q[c] * code[c] * 2^-9 over the 32 codes of 8 bytes (w.x, w.y)
+__device__ __forceinline__ float dot32_fp8_2b(const uint4 w, const float* q) {
+    float a0 = 0.f, a1 = 0.f;
+    float c[16];
+    codes16_fp8_2b(w.x, c);
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+        a0 = fmaf(c[e], q[e], a0);
+        a1 = fmaf(c[e + 1], q[e + 1], a1);
+    }
+    codes16_fp8_2b(w.y, c);
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+        a0 = fmaf(c[e], q[16 + e], a0);
+        a1 = fmaf(c[e + 1], q[16 + e + 1], a1);
+    }
+    return a0 + a1;
+}
+
+// acc[c] += wt * code[c] * 2^-9 for the 32 codes of 8 bytes (w.x, w.y)
+__device__ __forceinline__ void axpy32_fp8_2b(const uint4 w, float wt, float* acc) {
+    float c[16];
+    codes16_fp8_2b(w.x, c);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = fmaf(c[e], wt, acc[e]);
+    codes16_fp8_2b(w.y, c);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[16 + e] = fmaf(c[e], wt, acc[16 + e]);
+}
+
+// 32 channels of one lane at BITS bits: dot with q / axpy into acc (codes times 2^-9)
+template <int BITS>
+__device__ __forceinline__ float dot32_bits(const uint4 w, const float* q) {
+    if constexpr (BITS == 4) return dot32_fp8(w, q);
+    else return dot32_fp8_2b(w, q);
+}
+template <int BITS>
+__device__ __forceinline__ void axpy32_bits(const uint4 w, float wt, float* acc) {
+    if constexpr (BITS == 4) axpy32_fp8(w, wt, acc);
+    else axpy32_fp8_2b(w, wt, acc);
+}
+
 // Merge of split-softmax partials of one (sequence, head), laid out as n records of
 // `stride` floats: [max, sum, a[0..D), (b[0..D) if HAS_B)], by NW waves.
 // Every wave forms the global max M and L = sum_s sum_s * exp(max_s - M) itself: lanes
@@ -397,6 +463,41 @@ __device__ __forceinline__ uint4 ld_stream_u4(const void* p) {
     typedef unsigned v4 __attribute__((ext_vector_type(4)));
     const v4 v = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream_u2(const void* p) {
+    typedef unsigned v2 __attribute__((ext_vector_type(2)));
+    const v2 v = __builtin_nontemporal_load(reinterpret_cast<const v2*>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ld_stream_u16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+}
+// A lane's 32 channels of codes at BITS bits (16 bytes, or 8 in .x, .y)
+template <int BITS>
+__device__ __forceinline__ uint4 ld_codes32(const uint8_t* p) {
+    if constexpr (BITS == 4) return ld_stream_u4(p);
+    else {
+        const uint2 v = ld_stream_u2(p);
+        return make_uint4(v.x, v.y, 0u, 0u);
+    }
+}
+// A lane's 8 channels of codes at BITS bits (4 bytes, or 2), as the low bits of a word
+template <int BITS>
+__device__ __forceinline__ uint32_t ld_codes8(const uint8_t* p) {
+    if constexpr (BITS == 4) return ld_stream_u32(p);
+    else return ld_stream_u16(p);
+}
+// 8 codes of a word (4-bit: channel 2i low / 2i + 1 high nibble of byte i; 2-bit: channel
+// 4i + m in bits 2m of byte i) as floats
+template <int BITS>
+__device__ __forceinline__ void codes8_bits(uint32_t w, float* c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if constexpr (BITS == 4)
+            c[i] = (float)((w >> (4 * i)) & 15u);
+        else
+            c[i] = (float)((w >> (2 * i)) & 3u);
+    }
 }
 
 }  // namespace qkv

@@ -35,9 +35,9 @@ __device__ __forceinline__ float block_reduce_sum(float v, float* red) {
 }
 
 // Folded query of one key block: qp[c] = 2^9 * q[c] * s[c] (LDS), returns sum_c q[c] z[c].
-template <int D>
+template <int D, int BITS>
 __device__ __forceinline__ float fold_query(const uint8_t* bp, const float* qsh, float* qp, int lane) {
-    const float* km = reinterpret_cast<const float*>(bp + Block<D>::kKm);
+    const float* km = reinterpret_cast<const float*>(bp + Block<D, BITS>::kKm);
     float bias = 0.f;
 #pragma unroll
     for (int c = lane; c < D; c += 64) {
@@ -50,15 +50,15 @@ __device__ __forceinline__ float fold_query(const uint8_t* bp, const float* qsh,
 
 // K pass over one 64-slot block with the folded query computed here (planes that are not
 // prepared per split): calls emit(row, partial_logit) on one lane per row.
-template <int D, typename Emit>
+template <int D, int BITS, typename Emit>
 __device__ __forceinline__ void kpass_block(const uint8_t* bp, const float* qsh, float* qp_lds, int lane, int prt,
                                             int rsub, Emit emit) {
-    constexpr int LPR = Block<D>::kLpr, RPI = Block<D>::kRpi, NLD = 64 / RPI;
+    using Bk = Block<D, BITS>;
+    constexpr int LPR = Bk::kLpr, RPI = Bk::kRpi, NLD = 64 / RPI;
     uint4 w[NLD];
 #pragma unroll
-    for (int it = 0; it < NLD; ++it)
-        w[it] = ld_stream_u4(bp + Block<D>::kKc + (rsub + RPI * it) * (D / 2) + prt * 16);
-    const float bias = fold_query<D>(bp, qsh, qp_lds, lane);
+    for (int it = 0; it < NLD; ++it) w[it] = ld_codes32<BITS>(bp + Bk::kc(rsub + RPI * it) + prt * Bk::kLaneBytes);
+    const float bias = fold_query<D, BITS>(bp, qsh, qp_lds, lane);
     wave_sync_lds();
     float qp[32];
 #pragma unroll
@@ -69,29 +69,30 @@ __device__ __forceinline__ void kpass_block(const uint8_t* bp, const float* qsh,
     wave_sync_lds();
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
-        const float v = group_sum<LPR>(dot32_fp8(w[it], qp));
+        const float v = group_sum<LPR>(dot32_bits<BITS>(w[it], qp));
         if (prt == 0) emit(rsub + RPI * it, v + bias);
     }
 }
 
 // V pass over one block: weight(row) returns the row's probability (0 to skip).
-template <int D, typename Weight>
+template <int D, int BITS, typename Weight>
 __device__ __forceinline__ void vpass_block(const uint8_t* bp, int prt, int rsub, float* acc, float& vb,
                                             Weight weight) {
-    constexpr int RPI = Block<D>::kRpi, NLD = 64 / RPI;
+    using Bk = Block<D, BITS>;
+    constexpr int RPI = Bk::kRpi, NLD = 64 / RPI;
     uint4 w[NLD];
     float2 m[NLD];
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
         const int row = rsub + RPI * it;
-        w[it] = ld_stream_u4(bp + Block<D>::vc(row) + prt * 16);
-        m[it] = ld_stream_f2(bp + Block<D>::vm(row) + (prt >> 1) * 8);
+        w[it] = ld_codes32<BITS>(bp + Bk::vc(row) + prt * Bk::kLaneBytes);
+        m[it] = ld_stream_f2(bp + Bk::vm(row) + (prt >> 1) * 8);
     }
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
         const float pw = weight(rsub + RPI * it);
         vb = fmaf(pw, m[it].y, vb);
-        axpy32_fp8(w[it], pw * m[it].x * kFp8CodeScale, acc);
+        axpy32_bits<BITS>(w[it], pw * m[it].x * kFp8CodeScale, acc);
     }
 }
 
@@ -100,11 +101,18 @@ __device__ __forceinline__ void vpass_block(const uint8_t* bp, int prt, int rsub
 // by one.  Three waves per SIMD (the plan's three workgroups per CU) leave up to 168 VGPRs
 // per wave.  With its plane loads on the streaming policy the two-plane kernel compiles to
 // 128, but four workgroups per CU made the decode step slower.
-template <int D, int NPRE>
+// RB: code width of the residual planes (planes >= 1).  REPLACE (the full-state codec,
+// whose planes hold whole K/V states, not residuals): a column's key and value are those of
+// the last plane that stores it, so later planes overwrite logits instead of adding to
+// them, and in the V pass the deepest plane storing a position takes its probability (the
+// host passes the planes from the last dense one on, which then stores every position).
+template <int D, int NPRE, int RB, bool REPLACE>
 __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                           NewRow nr, float sm, float* __restrict__ scores, int ld,
                                                           float* __restrict__ part, int nsplit, int spb) {
+    static_assert(!REPLACE || (NPRE == 1 && RB == 4), "full-state planes: one prepared plane, 4-bit codes");
     constexpr int LPR = Block<D>::kLpr, RPI = Block<D>::kRpi, NLD = 64 / RPI;
+    constexpr int RBITS = REPLACE ? 4 : RB;  // code width of the planes after the first
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: block addresses stay scalar
@@ -141,15 +149,22 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
     // the join): a wave without blocks loads a valid block it does not use.
     const int blkP = max(0, min(blkA, blk1 - 1));
 
-    // Codes of a block of the prepared planes: K codes, V codes + per-row V meta.
+    // Codes of a block of the prepared planes: K codes, V codes + per-row V meta.  Plane p's
+    // code width is 4 bits for p = 0 and RBITS after it (compile-time once unrolled).
     uint4 wk[NPRE][NLD];
     auto load_k = [&](int blk) {
 #pragma unroll
         for (int p = 0; p < NPRE; ++p) {
-            const uint8_t* bp = block_ptr<D>(ca.p[p], ca.H, b, h, blk);
 #pragma unroll
-            for (int it = 0; it < NLD; ++it)
-                wk[p][it] = ld_stream_u4(bp + Block<D>::kKc + (rsub + RPI * it) * (D / 2) + prt * 16);
+            for (int it = 0; it < NLD; ++it) {
+                const int row = rsub + RPI * it;
+                if (p == 0 || RBITS == 4)
+                    wk[p][it] = ld_codes32<4>(block_ptr<D, 4>(ca.p[p], ca.H, b, h, blk) + Block<D, 4>::kc(row) +
+                                              prt * Block<D, 4>::kLaneBytes);
+                else
+                    wk[p][it] = ld_codes32<RBITS>(block_ptr<D, RBITS>(ca.p[p], ca.H, b, h, blk) +
+                                                  Block<D, RBITS>::kc(row) + prt * Block<D, RBITS>::kLaneBytes);
+            }
         }
     };
     for (int c = tid; c < D; c += 256) qsh[c] = bf16_to_f32(q[(size_t)bh * D + c]) * sm;
@@ -178,8 +193,10 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
             for (int u = 0; u < kFold; ++u) {
                 const int bb = wave + 4 * u;
                 if (bb < nb) {
-                    const float* km = reinterpret_cast<const float*>(block_ptr<D>(ca.p[p], ca.H, b, h, blk0 + bb) +
-                                                                     Block<D>::kKm);
+                    const float* km = reinterpret_cast<const float*>(
+                        (p == 0 || RBITS == 4)
+                            ? block_ptr<D, 4>(ca.p[p], ca.H, b, h, blk0 + bb) + Block<D, 4>::kKm
+                            : block_ptr<D, RBITS>(ca.p[p], ca.H, b, h, blk0 + bb) + Block<D, RBITS>::kKm);
 #pragma unroll
                     for (int cc = 0; cc < CPL; ++cc) {
                         fs[p][u][cc] = ld_stream_f32(km + lane + 64 * cc);
@@ -234,7 +251,8 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
                     qp[k] = t.x; qp[k + 1] = t.y; qp[k + 2] = t.z; qp[k + 3] = t.w;
                 }
 #pragma unroll
-                for (int it = 0; it < NLD; ++it) lg[it] += dot32_fp8(wk[p][it], qp);
+                for (int it = 0; it < NLD; ++it)
+                    lg[it] += (p == 0 || RBITS == 4) ? dot32_bits<4>(wk[p][it], qp) : dot32_bits<RBITS>(wk[p][it], qp);
                 bias += bpre[p][bb];
             }
 #pragma unroll
@@ -244,26 +262,29 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
             }
         }
         __syncthreads();
-        // K pass, remaining planes (sparse planes, or dense planes beyond the prepared ones)
+        // K pass, remaining planes (sparse planes, or dense planes beyond the prepared ones),
+        // in ascending order: their partial logits add up (or, full-state, overwrite)
         for (int p = npre; p < loop; ++p) {
             const PlaneArg& P = ca.p[p];
             if (P.dense) {
                 for (int blk = blk0 + wave; blk < blk1; blk += 4) {
-                    const uint8_t* bp = block_ptr<D>(P, ca.H, b, h, blk);
+                    const uint8_t* bp = block_ptr<D, RBITS>(P, ca.H, b, h, blk);
                     float* lg = logit + (blk - blk0) * 64;
-                    kpass_block<D>(bp, qsh, qps[wave], lane, prt, rsub, [&](int row, float v) { lg[row] += v; });
+                    kpass_block<D, RBITS>(bp, qsh, qps[wave], lane, prt, rsub, [&](int row, float v) {
+                        lg[row] = REPLACE ? v : lg[row] + v;
+                    });
                 }
             } else {
                 const int rs0 = P.rowstart[(size_t)b * nstart + blk0];
                 const int rs1 = P.rowstart[(size_t)b * nstart + blk1];
                 const int32_t* rp = P.rowpos + (size_t)b * P.n_blocks * 64;
                 for (int sb = (rs0 >> 6) + wave; sb * 64 < rs1 && sb < P.n_blocks; sb += 4) {
-                    const uint8_t* bp = block_ptr<D>(P, ca.H, b, h, sb);
-                    kpass_block<D>(bp, qsh, qps[wave], lane, prt, rsub, [&](int row, float v) {
+                    const uint8_t* bp = block_ptr<D, RBITS>(P, ca.H, b, h, sb);
+                    kpass_block<D, RBITS>(bp, qsh, qps[wave], lane, prt, rsub, [&](int row, float v) {
                         const int slot = sb * 64 + row;
                         if (slot >= rs0 && slot < rs1) {
                             const int pos = rp[slot] - j0;
-                            if (pos >= 0 && pos < L) logit[pos] += v;
+                            if (pos >= 0 && pos < L) logit[pos] = REPLACE ? v : logit[pos] + v;
                         }
                     });
                 }
@@ -302,12 +323,18 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
         auto load_v = [&](int blk) {
 #pragma unroll
             for (int p = 0; p < NPRE; ++p) {
-                const uint8_t* bp = block_ptr<D>(ca.p[p], ca.H, b, h, blk);
 #pragma unroll
                 for (int it = 0; it < NLD; ++it) {
                     const int row = rsub + RPI * it;
-                    wv[p][it] = ld_stream_u4(bp + Block<D>::vc(row) + prt * 16);
-                    mv[p][it] = ld_stream_f2(bp + Block<D>::vm(row) + (prt >> 1) * 8);
+                    if (p == 0 || RBITS == 4) {
+                        const uint8_t* bp = block_ptr<D, 4>(ca.p[p], ca.H, b, h, blk);
+                        wv[p][it] = ld_codes32<4>(bp + Block<D, 4>::vc(row) + prt * Block<D, 4>::kLaneBytes);
+                        mv[p][it] = ld_stream_f2(bp + Block<D, 4>::vm(row) + (prt >> 1) * 8);
+                    } else {
+                        const uint8_t* bp = block_ptr<D, RBITS>(ca.p[p], ca.H, b, h, blk);
+                        wv[p][it] = ld_codes32<RBITS>(bp + Block<D, RBITS>::vc(row) + prt * Block<D, RBITS>::kLaneBytes);
+                        mv[p][it] = ld_stream_f2(bp + Block<D, RBITS>::vm(row) + (prt >> 1) * 8);
+                    }
                 }
             }
         };
@@ -326,6 +353,51 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
         }
         lsum = block_reduce_sum(ls, red);
 
+        // V pass, remaining planes.  Residual codec: every plane adds its part of each stored
+        // position's value.  Full-state codec: the deepest plane storing a position takes its
+        // probability, so the planes run deepest first and each one clears the probabilities
+        // it used before the next (shallower) one, and finally the prepared plane, runs.
+        auto vpass_plane = [&](int p) {
+            const PlaneArg& P = ca.p[p];
+            if (P.dense) {
+                for (int blk = blk0 + wave; blk < blk1; blk += 4) {
+                    const uint8_t* bp = block_ptr<D, RBITS>(P, ca.H, b, h, blk);
+                    const float* lg = logit + (blk - blk0) * 64;
+                    vpass_block<D, RBITS>(bp, prt, rsub, acc, vb, [&](int row) { return lg[row]; });
+                }
+                if (REPLACE) {
+                    __syncthreads();
+                    for (int i = tid; i < L; i += 256) logit[i] = 0.f;
+                }
+            } else {
+                const int rs0 = P.rowstart[(size_t)b * nstart + blk0];
+                const int rs1 = P.rowstart[(size_t)b * nstart + blk1];
+                const int32_t* rp = P.rowpos + (size_t)b * P.n_blocks * 64;
+                for (int sb = (rs0 >> 6) + wave; sb * 64 < rs1 && sb < P.n_blocks; sb += 4) {
+                    const uint8_t* bp = block_ptr<D, RBITS>(P, ca.H, b, h, sb);
+                    vpass_block<D, RBITS>(bp, prt, rsub, acc, vb, [&](int row) {
+                        const int slot = sb * 64 + row;
+                        float pw = 0.f;
+                        if (slot >= rs0 && slot < rs1) {
+                            const int pos = rp[slot] - j0;
+                            if (pos >= 0 && pos < L) pw = logit[pos];
+                        }
+                        return pw;
+                    });
+                }
+                if (REPLACE) {
+                    __syncthreads();  // every wave has read the probabilities of this plane's positions
+                    for (int slot = rs0 + tid; slot < rs1; slot += 256) {
+                        const int pos = rp[slot] - j0;
+                        if (pos >= 0 && pos < L) logit[pos] = 0.f;
+                    }
+                }
+            }
+            if (REPLACE) __syncthreads();
+        };
+        if (REPLACE) {
+            for (int p = loop - 1; p >= npre; --p) vpass_plane(p);
+        }
         // V pass, prepared planes: every plane's codes of the block loaded together
         for (int blk = blkA; blk < blk1; blk += 4) {
             const int bb = blk - blk0;
@@ -337,36 +409,15 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
 #pragma unroll
                 for (int p = 0; p < NPRE; ++p) {
                     vb = fmaf(pw, mv[p][it].y, vb);
-                    axpy32_fp8(wv[p][it], pw * mv[p][it].x * kFp8CodeScale, acc);
+                    if (p == 0 || RBITS == 4)
+                        axpy32_bits<4>(wv[p][it], pw * mv[p][it].x * kFp8CodeScale, acc);
+                    else
+                        axpy32_bits<RBITS>(wv[p][it], pw * mv[p][it].x * kFp8CodeScale, acc);
                 }
             }
         }
-        // V pass, remaining planes
-        for (int p = npre; p < loop; ++p) {
-            const PlaneArg& P = ca.p[p];
-            if (P.dense) {
-                for (int blk = blk0 + wave; blk < blk1; blk += 4) {
-                    const uint8_t* bp = block_ptr<D>(P, ca.H, b, h, blk);
-                    const float* lg = logit + (blk - blk0) * 64;
-                    vpass_block<D>(bp, prt, rsub, acc, vb, [&](int row) { return lg[row]; });
-                }
-            } else {
-                const int rs0 = P.rowstart[(size_t)b * nstart + blk0];
-                const int rs1 = P.rowstart[(size_t)b * nstart + blk1];
-                const int32_t* rp = P.rowpos + (size_t)b * P.n_blocks * 64;
-                for (int sb = (rs0 >> 6) + wave; sb * 64 < rs1 && sb < P.n_blocks; sb += 4) {
-                    const uint8_t* bp = block_ptr<D>(P, ca.H, b, h, sb);
-                    vpass_block<D>(bp, prt, rsub, acc, vb, [&](int row) {
-                        const int slot = sb * 64 + row;
-                        float pw = 0.f;
-                        if (slot >= rs0 && slot < rs1) {
-                            const int pos = rp[slot] - j0;
-                            if (pos >= 0 && pos < L) pw = logit[pos];
-                        }
-                        return pw;
-                    });
-                }
-            }
+        if (!REPLACE) {
+            for (int p = npre; p < loop; ++p) vpass_plane(p);
         }
         }  // general path
         if (has_tail) {
@@ -484,16 +535,52 @@ size_t dense_ws_bytes(int B, int H, int D, int n_body) {
     return (size_t)B * H * pl.nsplit * (D + 2) * sizeof(float);
 }
 
+// The planes a full-state read of loop `loop` needs: from the last dense plane at or before
+// it (which stores every position and overrides every earlier plane) to `loop`.  The
+// argument's planes and tails are shifted so that plane 0 is that dense plane; *loop_out is
+// the loop's index in the shifted argument.
+CacheArg full_state_view(const CacheArg& ca, int loop, int* loop_out) {
+    int pd = 0;
+    for (int p = 0; p < loop; ++p)
+        if (ca.p[p].dense) pd = p;
+    CacheArg v = ca;
+    for (int p = 0; p < QKV_MAX_LOOPS; ++p) {
+        const int src = p + pd;
+        v.p[p] = src < QKV_MAX_LOOPS ? ca.p[src] : PlaneArg{};
+        v.tail_k[p] = src < QKV_MAX_LOOPS ? ca.tail_k[src] : nullptr;
+        v.tail_v[p] = src < QKV_MAX_LOOPS ? ca.tail_v[src] : nullptr;
+    }
+    v.nplanes = ca.nplanes - pd;
+    v.smask = nullptr;  // its bits name the unshifted planes
+    *loop_out = loop - pd;
+    return v;
+}
+
 template <int D>
 static void launch_dense_d(const CacheArg& ca, int loop, const uint16_t* q, NewRow nr, float sm, uint16_t* o, float* o32,
                            float* scores, int ld, float* lse, float* part, hipStream_t st) {
     const DensePlan pl = dense_plan(ca.B, ca.H, ca.n_body);
     dim3 grid(pl.nsplit, ca.H, ca.B);
-    // plane 1 (the base) is always dense; plane 2 joins it when it is dense too
-    if (loop >= 2 && ca.p[1].dense)
-        dense_split_kernel<D, 2><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit, pl.spb);
-    else
-        dense_split_kernel<D, 1><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit, pl.spb);
+    if (ca.full) {
+        int lv = loop;
+        const CacheArg v = full_state_view(ca, loop, &lv);
+        dense_split_kernel<D, 1, 4, true><<<grid, 256, 0, st>>>(v, lv, q, nr, sm, scores, ld, part, pl.nsplit, pl.spb);
+    } else if (ca.rbits == 2) {
+        if (loop >= 2 && ca.p[1].dense)
+            dense_split_kernel<D, 2, 2, false><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit,
+                                                                    pl.spb);
+        else
+            dense_split_kernel<D, 1, 2, false><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit,
+                                                                    pl.spb);
+    } else {
+        // plane 1 (the base) is always dense; plane 2 joins it when it is dense too
+        if (loop >= 2 && ca.p[1].dense)
+            dense_split_kernel<D, 2, 4, false><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit,
+                                                                    pl.spb);
+        else
+            dense_split_kernel<D, 1, 4, false><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit,
+                                                                    pl.spb);
+    }
     dense_combine_kernel<D><<<ca.B * ca.H, 64 * kCombineWaves, 0, st>>>(part, pl.nsplit, o, o32, lse);
 }
 

@@ -7,18 +7,23 @@
 //
 // Exactness: every codec step is a single IEEE fp32 operation, as the oracle does it
 // (correctly rounded division, rint half-to-even, fmaf dequant, no contraction).
+#include <type_traits>
+
 #include "launch.h"
 
 #pragma clang fp contract(off)
 
 namespace qkv {
 
-// code = clamp(rint((x - z) / s), 0, 15), code 0 when s == 0, with the IEEE quotient.
+// code = clamp(rint((x - z) / s), 0, top), code 0 when s == 0, with the IEEE quotient
+// (top = 15 for 4-bit codes, 3 for 2-bit codes).
 // rs is an approximation of 1/s: the product t * rs is within 6e-6 of the quotient for the
 // quotients that occur here (|t / s| <= 16), so rint of it agrees with rint of the exact,
 // correctly rounded quotient unless that lies within 1.5e-5 of a half-integer; only then is
 // the division carried out.
+template <int BITS>
 __device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float rs) {
+    constexpr float top = (float)((1 << BITS) - 1);
     if (s == 0.f) return 0u;
     const float t = x - z;
     const float q = t * rs;
@@ -29,7 +34,7 @@ __device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float 
     else
         r = __builtin_rintf(q);
     r = r < 0.f ? 0.f : r;
-    r = r > 15.f ? 15.f : r;
+    r = r > top ? top : r;
     return (uint32_t)r;
 }
 
@@ -42,13 +47,18 @@ __device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float 
 // the four waves through LDS), values per row over each 64-channel group (shuffles among the
 // group's 8 lanes), and each thread stores its own code words and metadata into the block.
 // Four workgroups per CU (at most 128 VGPRs).
-template <int D>
-__global__ __launch_bounds__(256, 4) void encode_group_kernel(CacheArg ca, int loop, int pos0, int n_pos,
+// OUTB: code width of the plane written (4, or 2 for 2-bit residual planes); RB: code width
+// of the residual planes read back through the chain (plane 0 is 4-bit); nch: planes of the
+// chain (loop - 1; 0 for loop 1 and for the full-state codec, which quantizes X^(loop) itself).
+template <int D, int OUTB, int RB>
+__global__ __launch_bounds__(256, 4) void encode_group_kernel(CacheArg ca, int loop, int nch, int pos0, int n_pos,
                                                            const int32_t* __restrict__ act_pos,
                                                            const int32_t* __restrict__ n_act, int ld_act,
                                                            const uint16_t* __restrict__ ksrc,
                                                            const uint16_t* __restrict__ vsrc, int ld_src,
                                                            int32_t* __restrict__ rowpos) {
+    using Bo = Block<D, OUTB>;
+    constexpr float kTop = (float)((1 << OUTB) - 1);
     constexpr int CH = 8;                // channels per item
     constexpr int IPR = D / CH;          // items per row
     constexpr int NIT = 64 * IPR / 256;  // items per thread
@@ -66,9 +76,8 @@ __global__ __launch_bounds__(256, 4) void encode_group_kernel(CacheArg ca, int l
     const int base = dense ? pos0 : P.rowstart[(size_t)b * nstart + pos0 / 64];
     const int blk_idx = (base + r0) >> 6;
     if (blk_idx >= P.n_blocks) return;  // sparse plane full: rows beyond its capacity are not stored
-    uint8_t* blk = const_cast<uint8_t*>(block_ptr<D>(P, ca.H, b, h, blk_idx));
+    uint8_t* blk = const_cast<uint8_t*>(block_ptr<D, OUTB>(P, ca.H, b, h, blk_idx));
     const bool from_tail = (ksrc == nullptr);
-    const int nch = loop - 1;           // planes of the chain Xhat^(r-1)
     const size_t bh = (size_t)b * ca.H + h;
 
     __shared__ int spos[64];
@@ -139,12 +148,21 @@ __global__ __launch_bounds__(256, 4) void encode_group_kernel(CacheArg ca, int l
                         const int slot = ipos[i0 + u] >= 0 ? sslot[p * 64 + row] : -1;
                         cw[u] = 0;
                         if (slot >= 0) {
-                            const uint8_t* bq = block_ptr<D>(Q, ca.H, b, h, slot >> 6);
+                            // plane p's code width: 4 bits for the base, RB after it
+                            const bool b4 = (p == 0 || RB == 4);
+                            const uint8_t* bq = b4 ? block_ptr<D, 4>(Q, ca.H, b, h, slot >> 6)
+                                                   : block_ptr<D, RB>(Q, ca.H, b, h, slot >> 6);
                             const int rw = slot & 63;
-                            cw[u] = *reinterpret_cast<const uint32_t*>(
-                                bq + (kind ? Block<D>::vc(rw) : Block<D>::kKc + rw * (D / 2)) + c0 / 2);
+                            if (b4)
+                                cw[u] = *reinterpret_cast<const uint32_t*>(
+                                    bq + (kind ? Block<D, 4>::vc(rw) : Block<D, 4>::kc(rw)) + c0 / 2);
+                            else
+                                cw[u] = *reinterpret_cast<const uint16_t*>(
+                                    bq + (kind ? Block<D, RB>::vc(rw) : Block<D, RB>::kc(rw)) + c0 * RB / 8);
+                            const int kkm = b4 ? Block<D, 4>::kKm : Block<D, RB>::kKm;
+                            const int vmo = b4 ? Block<D, 4>::vm(rw) : Block<D, RB>::vm(rw);
                             if (kind == 0) {
-                                const float* m = reinterpret_cast<const float*>(bq + Block<D>::kKm) + c0;
+                                const float* m = reinterpret_cast<const float*>(bq + kkm) + c0;
                                 const float4 sa = *reinterpret_cast<const float4*>(m);
                                 const float4 sb = *reinterpret_cast<const float4*>(m + 4);
                                 const float4 za = *reinterpret_cast<const float4*>(m + D);
@@ -154,7 +172,7 @@ __global__ __launch_bounds__(256, 4) void encode_group_kernel(CacheArg ca, int l
                                 z8[u][0] = za.x; z8[u][1] = za.y; z8[u][2] = za.z; z8[u][3] = za.w;
                                 z8[u][4] = zb.x; z8[u][5] = zb.y; z8[u][6] = zb.z; z8[u][7] = zb.w;
                             } else {
-                                const float2 vm = *reinterpret_cast<const float2*>(bq + Block<D>::vm(rw) + (c0 >> 6) * 8);
+                                const float2 vm = *reinterpret_cast<const float2*>(bq + vmo + (c0 >> 6) * 8);
 #pragma unroll
                                 for (int c = 0; c < CH; ++c) {
                                     s8[u][c] = vm.x;
@@ -168,10 +186,10 @@ __global__ __launch_bounds__(256, 4) void encode_group_kernel(CacheArg ca, int l
                         const int it = i0 + u;
                         const int row = (tid + 256 * it) / IPR;
                         if (ipos[it] < 0 || sslot[p * 64 + row] < 0) continue;  // not stored in loop p+1: keeps loop p's value
+                        const bool b4 = (p == 0 || RB == 4);
 #pragma unroll
                         for (int c = 0; c < CH; ++c) {
-                            const uint32_t byte = (cw[u] >> (8 * (c >> 1))) & 0xFFu;
-                            const float code = (float)((c & 1) ? (byte >> 4) : (byte & 15u));
+                            const float code = (float)(b4 ? ((cw[u] >> (4 * c)) & 15u) : ((cw[u] >> (2 * c)) & 3u));
                             const float deq = __builtin_fmaf(code, s8[u][c], z8[u][c]);
                             acc[it][c] = (p == 0) ? deq : acc[it][c] + deq;
                         }
@@ -228,7 +246,7 @@ __global__ __launch_bounds__(256, 4) void encode_group_kernel(CacheArg ca, int l
                     bmx = red_mx[q][c0 + c] > bmx ? red_mx[q][c0 + c] : bmx;
                 }
                 float range = bmx - a;
-                float sc = range / 15.0f;
+                float sc = range / kTop;
                 sc = sc + 0.0f;
                 s[c] = sc;
                 z[c] = a + 0.0f;
@@ -240,14 +258,15 @@ __global__ __launch_bounds__(256, 4) void encode_group_kernel(CacheArg ca, int l
                 uint32_t w = 0;
                 if (row < nr) {
 #pragma unroll
-                    for (int e = 0; e < CH; e += 2)
-                        w |= (quant_code(x[it][e], s[e], z[e], rs[e]) |
-                              (quant_code(x[it][e + 1], s[e + 1], z[e + 1], rs[e + 1]) << 4)) << (4 * e);
+                    for (int e = 0; e < CH; ++e) w |= quant_code<OUTB>(x[it][e], s[e], z[e], rs[e]) << (OUTB * e);
                 }
-                *reinterpret_cast<uint32_t*>(blk + Block<D>::kKc + row * (D / 2) + c0 / 2) = w;
+                if (OUTB == 4)
+                    *reinterpret_cast<uint32_t*>(blk + Bo::kc(row) + c0 / 2) = w;
+                else
+                    *reinterpret_cast<uint16_t*>(blk + Bo::kc(row) + c0 * OUTB / 8) = (uint16_t)w;
             }
             if (tid < IPR) {
-                float* m = reinterpret_cast<float*>(blk + Block<D>::kKm) + c0;
+                float* m = reinterpret_cast<float*>(blk + Bo::kKm) + c0;
                 *reinterpret_cast<float4*>(m) = make_float4(s[0], s[1], s[2], s[3]);
                 *reinterpret_cast<float4*>(m + 4) = make_float4(s[4], s[5], s[6], s[7]);
                 *reinterpret_cast<float4*>(m + D) = make_float4(z[0], z[1], z[2], z[3]);
@@ -271,19 +290,21 @@ __global__ __launch_bounds__(256, 4) void encode_group_kernel(CacheArg ca, int l
                     mx = fmaxf(mx, __shfl_xor(mx, m, 64));
                 }
                 float range = mx - mn;
-                float sc = range / 15.0f;
+                float sc = range / kTop;
                 sc = sc + 0.0f;
                 const float zc = mn + 0.0f;
                 uint32_t w = 0;
                 if (row < nr) {
                     const float rs = __builtin_amdgcn_rcpf(sc);
 #pragma unroll
-                    for (int e = 0; e < CH; e += 2)
-                        w |= (quant_code(x[it][e], sc, zc, rs) | (quant_code(x[it][e + 1], sc, zc, rs) << 4)) << (4 * e);
+                    for (int e = 0; e < CH; ++e) w |= quant_code<OUTB>(x[it][e], sc, zc, rs) << (OUTB * e);
                 }
-                *reinterpret_cast<uint32_t*>(blk + Block<D>::vc(row) + c0 / 2) = w;
+                if (OUTB == 4)
+                    *reinterpret_cast<uint32_t*>(blk + Bo::vc(row) + c0 / 2) = w;
+                else
+                    *reinterpret_cast<uint16_t*>(blk + Bo::vc(row) + c0 * OUTB / 8) = (uint16_t)w;
                 if ((tid & 7) == 0)
-                    *reinterpret_cast<float2*>(blk + Block<D>::vm(row) + (c0 >> 6) * 8) =
+                    *reinterpret_cast<float2*>(blk + Bo::vm(row) + (c0 >> 6) * 8) =
                         make_float2(row < nr ? sc : 0.f, row < nr ? zc : 0.f);
             }
         }
@@ -367,13 +388,32 @@ int launch_encode(const CacheArg& ca, int D, int loop, int pos0, int n_pos, cons
     const int ngroups = (n_pos + 63) / 64;
     dim3 grid(2 * ngroups, ca.H, ca.B);  // a key and a value workgroup per group
     int32_t* rowpos = const_cast<int32_t*>(P.rowpos);
-    const size_t dyn = (size_t)(loop - 1) * 64 * sizeof(int);  // chain slots of the stored rows
-    if (D == 128)
-        encode_group_kernel<128><<<grid, 256, dyn, st>>>(ca, loop, pos0, n_pos, act_pos, n_act, ld_act, ksrc, vsrc,
-                                                         ld_src, rowpos);
-    else
-        encode_group_kernel<64><<<grid, 256, dyn, st>>>(ca, loop, pos0, n_pos, act_pos, n_act, ld_act, ksrc, vsrc,
-                                                        ld_src, rowpos);
+    // the chain Xhat^(loop-1) is rebuilt for residual planes only
+    const int nch = ca.full ? 0 : loop - 1;
+    const int outb = (loop == 1 || ca.full) ? 4 : ca.rbits;
+    const size_t dyn = (size_t)nch * 64 * sizeof(int);  // chain slots of the stored rows
+    auto go = [&](auto dc, auto oc, auto rc) {
+        constexpr int DD = decltype(dc)::value, OB = decltype(oc)::value, RBB = decltype(rc)::value;
+        encode_group_kernel<DD, OB, RBB><<<grid, 256, dyn, st>>>(ca, loop, nch, pos0, n_pos, act_pos, n_act, ld_act,
+                                                                ksrc, vsrc, ld_src, rowpos);
+    };
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    using B2 = std::integral_constant<int, 2>;
+    using B4 = std::integral_constant<int, 4>;
+    if (D == 128) {
+        if (ca.rbits == 2 && !ca.full) {
+            if (outb == 2) go(I128{}, B2{}, B2{}); else go(I128{}, B4{}, B2{});
+        } else {
+            go(I128{}, B4{}, B4{});
+        }
+    } else {
+        if (ca.rbits == 2 && !ca.full) {
+            if (outb == 2) go(I64{}, B2{}, B2{}); else go(I64{}, B4{}, B2{});
+        } else {
+            go(I64{}, B4{}, B4{});
+        }
+    }
     if (hipGetLastError() != hipSuccess) return QKV_ELAUNCH;
     if (!P.dense) {
         dim3 g2((n_pos + 255) / 256, ca.B);

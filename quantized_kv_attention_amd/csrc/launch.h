@@ -25,6 +25,9 @@ struct DensePlan {
     int nsplit;
 };
 DensePlan dense_plan(int B, int H, int n_body);
+// Full-state codec: the cache argument seen from the last dense plane at or before `loop`
+// (plane 0 of the result); *loop_out = the loop's index in it.
+CacheArg full_state_view(const CacheArg& ca, int loop, int* loop_out);
 size_t dense_ws_bytes(int B, int H, int D, int n_body);
 int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, uint16_t* o, float* o32,
                  float* scores, int ld, float* lse, void* ws, hipStream_t st);
@@ -35,6 +38,9 @@ int launch_dense_noalloc(const CacheArg& ca, int D, int loop, const uint16_t* q,
 size_t select_ws_bytes(int B, int H, int n);
 int launch_select(const float* scores, int ld, const float* lse, int B, int H, int n, int k, int32_t* idx,
                   float* p_sel, float* mass, void* ws, hipStream_t st);
+
+int launch_export_plane(const CacheArg& ca, int D, int loop, int b, int h, int n_slots, uint8_t* kc, uint8_t* vc,
+                        float* ks, float* kz, float* vs, float* vz, hipStream_t st);
 
 int launch_stream_read(const void* src, size_t n_bytes, uint32_t* sink, hipStream_t st);
 size_t sparse_ws_bytes(int B, int H, int D, int k);

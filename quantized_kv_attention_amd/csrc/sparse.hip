@@ -18,6 +18,8 @@
 // more waves in flight is what shortens it.
 // A second kernel merges the partials of each (sequence, head), writes o and shifts the
 // selected scores.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace qkv {
@@ -29,13 +31,28 @@ constexpr int chunk_cols(int D) { return kSpWaves * kWaveRounds * (64 / (D / 8))
 // A chunk's partial record: [max, sum, -, -, U[0..D), W[0..D)], 16-byte aligned.
 constexpr int sp_record(int D) { return 2 * D + 4; }
 
-__device__ __forceinline__ void codes8(uint32_t w, float* c) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const uint32_t byte = (w >> (8 * m)) & 0xFFu;
-        c[2 * m] = (float)(byte & 0xFu);
-        c[2 * m + 1] = (float)(byte >> 4);
-    }
+// One plane's data of a gathered slot for a lane's 8 channels c0..c0+7: key and value code
+// words (BITS bytes each), the key group's scales and zeros, the slot's value (s, z).
+struct SlotData {
+    uint32_t kw, vw;
+    float4 s0, s1, z0, z1;
+    float2 vm;
+};
+template <int D, int BITS>
+__device__ __forceinline__ SlotData load_slot(const PlaneArg& P, int H, int b, int h, int slot, int prt, int c0) {
+    using Bk = Block<D, BITS>;
+    const uint8_t* bp = block_ptr<D, BITS>(P, H, b, h, slot >> 6);
+    const int row = slot & 63;
+    SlotData d;
+    d.kw = ld_codes8<BITS>(bp + Bk::kc(row) + prt * BITS);
+    d.vw = ld_codes8<BITS>(bp + Bk::vc(row) + prt * BITS);
+    const float* km = reinterpret_cast<const float*>(bp + Bk::kKm) + c0;
+    d.s0 = *reinterpret_cast<const float4*>(km);
+    d.s1 = *reinterpret_cast<const float4*>(km + 4);
+    d.z0 = *reinterpret_cast<const float4*>(km + D);
+    d.z1 = *reinterpret_cast<const float4*>(km + D + 4);
+    d.vm = ld_stream_f2(bp + Bk::vm(row) + (c0 >> 6) * 8);
+    return d;
 }
 
 // Stores the newest position's row (nr, [B*H][D]) of (sequence, head) bh in tail ring slot
@@ -58,12 +75,16 @@ __device__ __forceinline__ void store_new_row(NewRow nr, uint16_t* tk, uint16_t*
 // together and then every plane's data of the batch together; a plane that does not store
 // the column loads its block 0 and weighs it 0, so every plane must hold a block.  It
 // runs at 3 waves per SIMD (up to 168 VGPRs).
-template <int D, int SB>
+// RB: code width of the residual planes (planes >= 1).  REPLACE (full-state codec): a
+// column's key and value are those of the last plane storing it, not the sum of the chain
+// (the host passes the planes from the last dense one before `loop` on).
+template <int D, int SB, int RB, bool REPLACE>
 __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 1) void sparse_chunk_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                            NewRow nr, float sm, const int32_t* __restrict__ idx,
                                                            const float* __restrict__ p_sel, int k,
                                                            float* __restrict__ cs,
                                                            float* __restrict__ part) {
+    constexpr int RBITS = REPLACE ? 4 : RB;  // code width of the planes after the first
     constexpr int LPC = D / 8;             // lanes per column
     constexpr int CPR = 64 / LPC;          // columns per wave round
     constexpr int ROUNDS = kWaveRounds;
@@ -198,50 +219,53 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 1) void sparse_chunk_ke
                                 sl[u] = P.rowmap[(size_t)b * cap + j];
                         }
                     }
-                    uint32_t kw[SB], vw[SB];
-                    float4 s0[SB], s1[SB], z0[SB], z1[SB];
-                    float2 vm[SB];
+                    SlotData sd[SB];
                     bool act[SB];
 #pragma unroll
                     for (int u = 0; u < SB; ++u) {
-                        const PlaneArg& P = ca.p[pp[u] >= 0 ? pp[u] : pp[0]];
+                        const int pu = pp[u] >= 0 ? pp[u] : pp[0];
+                        const PlaneArg& P = ca.p[pu];
                         act[u] = pp[u] >= 0 && sl[u] >= 0 && sl[u] < P.n_blocks * 64;
                         const int slot = act[u] ? sl[u] : 0;
-                        const uint8_t* bp = block_ptr<D>(P, ca.H, b, h, slot >> 6);
-                        const int row = slot & 63;
-                        kw[u] = ld_stream_u32(bp + Block<D>::kKc + row * (D / 2) + prt * 4);
-                        vw[u] = ld_stream_u32(bp + Block<D>::vc(row) + prt * 4);
-                        const float* km = reinterpret_cast<const float*>(bp + Block<D>::kKm) + c0;
-                        s0[u] = *reinterpret_cast<const float4*>(km);
-                        s1[u] = *reinterpret_cast<const float4*>(km + 4);
-                        z0[u] = *reinterpret_cast<const float4*>(km + D);
-                        z1[u] = *reinterpret_cast<const float4*>(km + D + 4);
-                        vm[u] = ld_stream_f2(bp + Block<D>::vm(row) + (c0 >> 6) * 8);
+                        if (pu == 0 || RBITS == 4)
+                            sd[u] = load_slot<D, 4>(P, ca.H, b, h, slot, prt, c0);
+                        else
+                            sd[u] = load_slot<D, RBITS>(P, ca.H, b, h, slot, prt, c0);
                     }
 #pragma unroll
                     for (int u = 0; u < SB; ++u) {
                         const int p = pp[u];
                         if (!act[u]) continue;
-                        const float ks[8] = {s0[u].x, s0[u].y, s0[u].z, s0[u].w, s1[u].x, s1[u].y, s1[u].z, s1[u].w};
-                        const float kz[8] = {z0[u].x, z0[u].y, z0[u].z, z0[u].w, z1[u].x, z1[u].y, z1[u].z, z1[u].w};
-                        float code[8];
-                        codes8(kw[u], code);
+                        const float ks[8] = {sd[u].s0.x, sd[u].s0.y, sd[u].s0.z, sd[u].s0.w,
+                                             sd[u].s1.x, sd[u].s1.y, sd[u].s1.z, sd[u].s1.w};
+                        const float kz[8] = {sd[u].z0.x, sd[u].z0.y, sd[u].z0.z, sd[u].z0.w,
+                                             sd[u].z1.x, sd[u].z1.y, sd[u].z1.z, sd[u].z1.w};
+                        float code[8], vcode[8];
+                        if (p == 0 || RBITS == 4) {
+                            codes8_bits<4>(sd[u].kw, code);
+                            codes8_bits<4>(sd[u].vw, vcode);
+                        } else {
+                            codes8_bits<RBITS>(sd[u].kw, code);
+                            codes8_bits<RBITS>(sd[u].vw, vcode);
+                        }
 #pragma unroll
                         for (int c = 0; c < 8; ++c) {
                             const float deq = fmaf(code[c], ks[c], kz[c]);
-                            kh[c] = (p == 0) ? deq : kh[c] + deq;
+                            kh[c] = (p == 0 || REPLACE) ? deq : kh[c] + deq;
                         }
-                        codes8(vw[u], code);
                         if (p < loop - 1) {
 #pragma unroll
                             for (int c = 0; c < 8; ++c) {
-                                const float deq = fmaf(code[c], vm[u].x, vm[u].y);
-                                vh[c] = (p == 0) ? deq : vh[c] + deq;
+                                const float deq = fmaf(vcode[c], sd[u].vm.x, sd[u].vm.y);
+                                vh[c] = (p == 0 || REPLACE) ? deq : vh[c] + deq;
                             }
                         } else {
                             act_r = true;
 #pragma unroll
-                            for (int c = 0; c < 8; ++c) vc[c] = vh[c] + fmaf(code[c], vm[u].x, vm[u].y);
+                            for (int c = 0; c < 8; ++c) {
+                                const float deq = fmaf(vcode[c], sd[u].vm.x, sd[u].vm.y);
+                                vc[c] = REPLACE ? deq : vh[c] + deq;
+                            }
                         }
                     }
                 }
@@ -264,36 +288,37 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 1) void sparse_chunk_ke
                         const PlaneArg& P = ca.p[p];
                         const int slot = sl[u];
                         if (slot < 0 || slot >= P.n_blocks * 64) continue;
-                        const uint8_t* bp = block_ptr<D>(P, ca.H, b, h, slot >> 6);
-                        const int row = slot & 63;
-                        const uint32_t kw = ld_stream_u32(bp + Block<D>::kKc + row * (D / 2) + prt * 4);
-                        const uint32_t vw = ld_stream_u32(bp + Block<D>::vc(row) + prt * 4);
-                        const float* km = reinterpret_cast<const float*>(bp + Block<D>::kKm) + c0;
-                        const float4 s0 = *reinterpret_cast<const float4*>(km);
-                        const float4 s1 = *reinterpret_cast<const float4*>(km + 4);
-                        const float4 z0 = *reinterpret_cast<const float4*>(km + D);
-                        const float4 z1 = *reinterpret_cast<const float4*>(km + D + 4);
-                        const float2 vm = ld_stream_f2(bp + Block<D>::vm(row) + (c0 >> 6) * 8);
-                        const float ks[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-                        const float kz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-                        float code[8];
-                        codes8(kw, code);
+                        SlotData sd;
+                        float code[8], vcode[8];
+                        if (p == 0 || RBITS == 4) {
+                            sd = load_slot<D, 4>(P, ca.H, b, h, slot, prt, c0);
+                            codes8_bits<4>(sd.kw, code);
+                            codes8_bits<4>(sd.vw, vcode);
+                        } else {
+                            sd = load_slot<D, RBITS>(P, ca.H, b, h, slot, prt, c0);
+                            codes8_bits<RBITS>(sd.kw, code);
+                            codes8_bits<RBITS>(sd.vw, vcode);
+                        }
+                        const float ks[8] = {sd.s0.x, sd.s0.y, sd.s0.z, sd.s0.w, sd.s1.x, sd.s1.y, sd.s1.z, sd.s1.w};
+                        const float kz[8] = {sd.z0.x, sd.z0.y, sd.z0.z, sd.z0.w, sd.z1.x, sd.z1.y, sd.z1.z, sd.z1.w};
 #pragma unroll
                         for (int c = 0; c < 8; ++c) {
                             const float deq = fmaf(code[c], ks[c], kz[c]);
-                            kh[c] = (p == 0) ? deq : kh[c] + deq;
+                            kh[c] = (p == 0 || REPLACE) ? deq : kh[c] + deq;
                         }
-                        codes8(vw, code);
                         if (p < loop - 1) {
 #pragma unroll
                             for (int c = 0; c < 8; ++c) {
-                                const float deq = fmaf(code[c], vm.x, vm.y);
-                                vh[c] = (p == 0) ? deq : vh[c] + deq;
+                                const float deq = fmaf(vcode[c], sd.vm.x, sd.vm.y);
+                                vh[c] = (p == 0 || REPLACE) ? deq : vh[c] + deq;
                             }
                         } else {
                             act_r = true;
 #pragma unroll
-                            for (int c = 0; c < 8; ++c) vc[c] = vh[c] + fmaf(code[c], vm.x, vm.y);
+                            for (int c = 0; c < 8; ++c) {
+                                const float deq = fmaf(vcode[c], sd.vm.x, sd.vm.y);
+                                vc[c] = REPLACE ? deq : vh[c] + deq;
+                            }
                         }
                     }
                 }
@@ -519,24 +544,38 @@ int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow
     float* part = static_cast<float*>(ws);
     float* cs = scores ? part + (size_t)ca.B * ca.H * nchunk * sp_record(D) : nullptr;  // raw scores for the splice
     dim3 grid(nchunk, ca.H, ca.B);
+    // full-state codec: the planes from the last dense one before `loop` on
+    int lv = loop;
+    const CacheArg v = ca.full ? full_state_view(ca, loop - 1, &lv) : ca;
+    if (ca.full) lv += 1;  // the view was taken for loop - 1
     // deep chains: batched loads (and long chains first), which need every plane of the
     // chain to hold a block
-    bool batched = loop > 4;
-    for (int p = 0; batched && p < loop; ++p) batched = ca.p[p].data != nullptr && ca.p[p].n_blocks > 0;
+    bool batched = lv > 4;
+    for (int p = 0; batched && p < lv; ++p) batched = v.p[p].data != nullptr && v.p[p].n_blocks > 0;
+    auto chunks = [&](auto dc, auto rbc, auto fullc) {
+        constexpr int DD = decltype(dc)::value, RBB = decltype(rbc)::value;
+        constexpr bool FF = decltype(fullc)::value;
+        if (!batched)
+            sparse_chunk_kernel<DD, 1, RBB, FF><<<grid, 64 * kSpWaves, 0, st>>>(v, lv, q, nr, sm, idx, p_sel, k, cs, part);
+        else
+            sparse_chunk_kernel<DD, 3, RBB, FF><<<grid, 64 * kSpWaves, 0, st>>>(v, lv, q, nr, sm, idx, p_sel, k, cs, part);
+        sparse_combine_kernel<DD><<<ca.B * ca.H, 64 * kSpCombineWaves, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs,
+                                                                              k, scores, ld, o, o32);
+    };
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    using B2 = std::integral_constant<int, 2>;
+    using B4 = std::integral_constant<int, 4>;
+    using T = std::true_type;
+    using F = std::false_type;
     if (D == 128) {
-        if (!batched)
-            sparse_chunk_kernel<128, 1><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
-        else
-            sparse_chunk_kernel<128, 3><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
-        sparse_combine_kernel<128><<<ca.B * ca.H, 64 * kSpCombineWaves, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
-                                                                              scores, ld, o, o32);
+        if (ca.full) chunks(I128{}, B4{}, T{});
+        else if (ca.rbits == 2) chunks(I128{}, B2{}, F{});
+        else chunks(I128{}, B4{}, F{});
     } else {
-        if (!batched)
-            sparse_chunk_kernel<64, 1><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
-        else
-            sparse_chunk_kernel<64, 3><<<grid, 64 * kSpWaves, 0, st>>>(ca, loop, q, nr, sm, idx, p_sel, k, cs, part);
-        sparse_combine_kernel<64><<<ca.B * ca.H, 64 * kSpCombineWaves, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs, k,
-                                                                             scores, ld, o, o32);
+        if (ca.full) chunks(I64{}, B4{}, T{});
+        else if (ca.rbits == 2) chunks(I64{}, B2{}, F{});
+        else chunks(I64{}, B4{}, F{});
     }
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
 }

@@ -1,6 +1,6 @@
 """Helpers of the GPU parity tests: run the HIP path and the oracle on the same seeded
-inputs and compare them.  The packed plane layout is read back from the documented byte
-layout (include/qkv_attn.h) so that codes and metadata compare as logical content."""
+inputs and compare them.  Planes are read back through the library's qkv_export_plane, so
+codes and metadata compare as logical content, whatever the packed layout."""
 from __future__ import annotations
 
 import math
@@ -32,31 +32,11 @@ def bf16_tensor_to_f32(t: torch.Tensor) -> np.ndarray:
 
 
 def unpack_plane(cache: qcache.LayerCache, r: int, b: int, h: int, nslots: int):
-    """Logical content of slots [0, nslots) of loop r+1's plane for (b, h)."""
-    d = cache.d
-    bb = cache.block_bytes
-    nblk_all = cache.desc.plane[r].n_blocks
-    nb = (nslots + 63) // 64
-    raw = cache.planes[r].view(cache.B, cache.H, nblk_all, bb)[b, h, :nb].cpu().numpy()
-    def nib(x):
-        x = x.reshape(nb * 64, d // 2)
-        out = np.empty((nb * 64, d), np.uint8)
-        out[:, 0::2] = x & 15
-        out[:, 1::2] = x >> 4
-        return out
-    g = d // 64
-    kc = nib(raw[:, 0:32 * d])
-    if d == 128:  # value records: 64 code bytes + (s, z) per group, per slot; then key meta
-        rec = raw[:, 32 * d:32 * d + 64 * (d // 2 + 8 * g)].reshape(nb, 64, d // 2 + 8 * g)
-        vc = nib(np.ascontiguousarray(rec[:, :, :d // 2]))
-        vm = np.ascontiguousarray(rec[:, :, d // 2:]).view(np.float32).reshape(nb * 64, g, 2)
-        km0 = 32 * d + 64 * (d // 2 + 8 * g)
-    else:
-        vc = nib(raw[:, 32 * d:64 * d])
-        vm = np.ascontiguousarray(raw[:, 72 * d:72 * d + 64 * g * 8]).view(np.float32).reshape(nb * 64, g, 2)
-        km0 = 64 * d
-    km = np.ascontiguousarray(raw[:, km0:km0 + 8 * d]).view(np.float32).reshape(nb, 2, d)
-    return dict(kc=kc[:nslots], vc=vc[:nslots], ks=km[:, 0], kz=km[:, 1], vs=vm[:nslots, :, 0], vz=vm[:nslots, :, 1])
+    """Logical content of slots [0, nslots) of loop r+1's plane for (b, h), unpacked by the
+    library's qkv_export_plane (one code per byte, fp32 metadata)."""
+    out = qkv.export_plane(cache, r + 1, b, h, nslots)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
 
 
 def compare_planes(cache: qcache.LayerCache, oc: orc.OracleCache, heads_gpu, heads_orc, loops=None):
@@ -98,7 +78,8 @@ def assert_out(o_gpu_bf16, o_ref_f64, what):
 class Pair:
     """GPU cache + oracle cache built from the same seeded inputs."""
 
-    def __init__(self, w: synth.Workload, n=None, heads=None, extra=0, dense=None, oracle_heads=None):
+    def __init__(self, w: synth.Workload, n=None, heads=None, extra=0, dense=None, oracle_heads=None,
+                 residual_bits=4, full_state=False):
         self.w = w
         self.n = w.n if n is None else n
         self.heads = list(range(w.H)) if heads is None else list(heads)
@@ -109,9 +90,11 @@ class Pair:
         self.act = act
         cap = int(math.ceil((self.n + extra + 64) / 64) * 64)
         self.dense = [w.rho[r] >= 1.0 for r in range(w.R)] if dense is None else dense
-        self.gpu = qcache.LayerCache(w.B, H, w.d, w.R, cap, dense=self.dense)
+        self.gpu = qcache.LayerCache(w.B, H, w.d, w.R, cap, dense=self.dense, residual_bits=residual_bits,
+                                     full_state=full_state)
         self.gpu.prefill([to_dev_bf16(k) for k in K], [to_dev_bf16(v) for v in V], act)
-        self.orc = orc.OracleCache(w.B, len(self.oh), w.d, w.R, cap)
+        self.orc = orc.OracleCache(w.B, len(self.oh), w.d, w.R, cap, residual_bits=residual_bits,
+                                   full_state=full_state)
         self.orc.prefill([k[:, self.oh] for k in K], [v[:, self.oh] for v in V], act)
         del K, V
         self.bufs = qcache.DecodeBuffers(self.gpu, max_k=self.n + extra)

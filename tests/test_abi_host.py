@@ -28,6 +28,8 @@ def test_exports_every_declared_symbol():
 
 def test_sizes():
     assert qkv.block_bytes(128) == 10240 and qkv.block_bytes(64) == 5120 and qkv.block_bytes(96) == 0
+    # 2-bit planes: codes take half the bytes, metadata the same
+    assert qkv.block_bytes(128, 2) == 6144 and qkv.block_bytes(64, 2) == 3072 and qkv.block_bytes(128, 3) == 0
     assert qkv.body_len(0) == 0 and qkv.body_len(127) == 0 and qkv.body_len(256) == 192
     assert qkv.body_len(32768) == 32704
     assert qkv.workspace_bytes(1, 16, 128, 32768, 3277) > 16 * (512 + 1) * 130 * 4 * 0
@@ -104,6 +106,15 @@ def test_argument_validation():
     assert L.qkv_stream_read(vp(16), 40, vp(16), None) == qkv.QKV_EINVAL
     assert L.qkv_stream_read(vp(24), 64, vp(16), None) == qkv.QKV_EINVAL
     assert L.qkv_stream_read(vp(16), 64, vp(20), None) == qkv.QKV_EINVAL
+    # plane export: loop, sequence or head out of range, more slots than the plane holds
+    assert L.qkv_export_plane(ctypes.byref(d), 3, 0, 0, 64, *[vp(16)] * 6, None) == qkv.QKV_EINVAL
+    assert L.qkv_export_plane(ctypes.byref(d), 1, 1, 0, 64, *[vp(16)] * 6, None) == qkv.QKV_EINVAL
+    assert L.qkv_export_plane(ctypes.byref(d), 1, 0, 1, 64, *[vp(16)] * 6, None) == qkv.QKV_EINVAL
+    assert L.qkv_export_plane(ctypes.byref(d), 1, 0, 0, 257, *[vp(16)] * 6, None) == qkv.QKV_EINVAL
+    # codec fields: 3-bit residuals are unsupported; the full-state codec is 4-bit only
+    assert L.attn_decode_dense(ctypes.byref(_desc(residual_bits=3)), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EUNSUPPORTED
+    assert L.attn_decode_dense(ctypes.byref(_desc(residual_bits=2, full_state=1)), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EUNSUPPORTED
+    assert L.attn_decode_dense(ctypes.byref(_desc(full_state=2)), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
@@ -121,6 +132,12 @@ def test_host_buffers_and_descriptor_cpu():
     assert c.desc.plane[0].n_blocks == 8 and c.desc.plane[2].dense == 0
     assert c.desc.plane[2].rowmap == c.rowmap[2].data_ptr()
     assert c.planes[0].numel() == 2 * 3 * 8 * qkv.block_bytes(128)
+    # 2-bit residual planes: the base keeps 4-bit blocks, later planes take 2-bit ones
+    c2 = qcache.LayerCache(1, 2, 128, 4, 256, device="cpu", residual_bits=2)
+    assert c2.desc.residual_bits == 2 and c2.bits == [4, 2, 2, 2]
+    assert c2.planes[0].numel() == 2 * 4 * 10240 and c2.planes[1].numel() == 2 * 4 * 6144
+    c3 = qcache.LayerCache(1, 2, 64, 4, 256, device="cpu", full_state=True)
+    assert c3.desc.full_state == 1 and c3.bits == [4, 4, 4, 4]
     b = qcache.DecodeBuffers(c, max_k=50, device="cpu")
     idx, ps, m = b.selection(3, 50)
     assert idx.shape == (2, 3, 50) and ps.shape == (2, 3, 50) and m.shape == (2, 3)
