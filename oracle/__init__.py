@@ -63,6 +63,8 @@ def lib():
         L.orc_attend_sparse.argtypes = [ctypes.c_int, ctypes.c_int, f32p, ctypes.c_double, f32p, f32p, f32p,
                                         i32p, ctypes.c_int, f64p, ctypes.c_double, f64p, ctypes.c_double, f64p, f64p]
         L.orc_attend_sparse.restype = None
+        L.orc_token_change.argtypes = [ctypes.c_int, ctypes.c_int, f32p, f32p, u8p, f64p]
+        L.orc_token_change.restype = None
         _lib = L
     return _lib
 
@@ -188,6 +190,36 @@ def attend_sparse(q, Kr, Vr, Vrm1, idx, p_sel, mass: float, o_prev, lse: float, 
                             _p(p_sel, ctypes.c_double), float(mass), _p(o_prev, ctypes.c_double),
                             float(lse), _p(sc, ctypes.c_double), _p(o, ctypes.c_double))
     return o, sc
+
+
+# ----------------------------------------------------------------------------------
+# Token selection (explainer section 3, cross-loop token-sparse updates; project page
+# STEP 01): rank the tokens active in the preceding loop by their normalized hidden-state
+# change and keep the top k; the kept set is the next loop's active set.
+# ----------------------------------------------------------------------------------
+def token_change(H_cur, H_prev, act_prev=None):
+    """fp64 score per token: ||H_cur - H_prev|| / ||H_prev|| (see orc_token_change); -inf
+    for tokens outside act_prev (bool [n], None = every token)."""
+    Hc = np.ascontiguousarray(H_cur, np.float32)
+    Hp = np.ascontiguousarray(H_prev, np.float32)
+    n, dm = Hc.shape
+    out = np.zeros(n, np.float64)
+    a = None if act_prev is None else np.ascontiguousarray(act_prev, np.uint8)
+    lib().orc_token_change(n, dm, _p(Hc, ctypes.c_float), _p(Hp, ctypes.c_float),
+                           None if a is None else _p(a, ctypes.c_uint8), _p(out, ctypes.c_double))
+    return out
+
+
+def select_tokens(H_cur, H_prev, act_prev, k: int, scores_f32=None):
+    """The next loop's active tokens, ascending: the min(k, |act_prev|) tokens of act_prev
+    with the largest change score, ties to the lower index.  The ranking key is the score
+    rounded to fp32, or `scores_f32` when given (to compare on identical scores)."""
+    sc = token_change(H_cur, H_prev, act_prev).astype(np.float32) if scores_f32 is None else \
+        np.asarray(scores_f32, np.float32)
+    n_prev = int(np.asarray(act_prev).sum()) if act_prev is not None else sc.shape[0]
+    kk = min(int(k), n_prev)
+    idx, _, _ = select(sc, 0.0, kk)
+    return idx
 
 
 # ----------------------------------------------------------------------------------

@@ -242,3 +242,29 @@ void orc_attend_sparse(int n, int d, const float* q, double sm,
     }
     free(s);
 }
+
+/* ---------------------------------------------------------------------------------
+ * Token selection score [P5 section 3 "Cross-loop token-sparse updates": after the dense
+ * loops, each loop ranks the tokens updated in the preceding loop by their normalized
+ * hidden-state change and keeps a top-k subset; P2 STEP 01].  Reading: the change of
+ * token t is the relative one, ||H_cur[t] - H_prev[t]||_2 / ||H_prev[t]||_2, in fp64
+ * (a zero previous state gives +inf for a nonzero change and 0 otherwise).  Tokens not
+ * active in the preceding loop (act_prev[t] == 0) score -inf, so the sets nest.
+ *   H_cur, H_prev [n][dm]: the preceding loop's output and input states (bf16 values
+ *   held in fp32); score[n] out.
+ * ------------------------------------------------------------------------------- */
+void orc_token_change(int n, int dm, const float* H_cur, const float* H_prev, const uint8_t* act_prev,
+                      double* score)
+{
+    for (int t = 0; t < n; ++t) {
+        if (act_prev && !act_prev[t]) { score[t] = -INFINITY; continue; }
+        double dd = 0.0, pp = 0.0;
+        for (int c = 0; c < dm; ++c) {
+            double a = (double)H_cur[(long)t * dm + c], b = (double)H_prev[(long)t * dm + c];
+            dd += (a - b) * (a - b);
+            pp += b * b;
+        }
+        if (pp > 0.0) score[t] = sqrt(dd) / sqrt(pp);
+        else score[t] = dd > 0.0 ? INFINITY : 0.0;
+    }
+}

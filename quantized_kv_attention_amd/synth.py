@@ -25,7 +25,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-KIND_KV, KIND_MASK, KIND_Q, KIND_NEW = 1, 2, 3, 4
+KIND_KV, KIND_MASK, KIND_Q, KIND_NEW, KIND_HIDDEN = 1, 2, 3, 4, 5
 
 
 @dataclass
@@ -222,3 +222,19 @@ def gen_layer_torch(w: Workload, layer: int, device="cuda", n: int | None = None
         V.append(torch.where(a, (V[r - 1].float() + sig * nv).to(torch.bfloat16), V[r - 1]))
         del nv
     return K, V, act
+
+
+def gen_hidden(w: Workload, dm: int, n: int | None = None, b: int = 0):
+    """Per-loop hidden states of one sequence for the token selection: H[r] uint16 (bf16
+    bits) [n, dm], r = 0..R-1.  H^(1) ~ N(0, 1); loop r's update of token t has magnitude
+    sigma_r * g_t with g_t log-normal (sigma 1.5), so that a minority of tokens carries most
+    of the change, as the explainer's section 2 describes the token-update redundancy."""
+    n = w.n if n is None else n
+    g = _rng(w.seed, KIND_HIDDEN, b)
+    H = [bf16_round_bits(g.standard_normal((n, dm), dtype=np.float32))]
+    gt = np.exp(1.5 * g.standard_normal(n)).astype(np.float32)
+    for r in range(1, w.R):
+        sig = np.float32(w.sigma[r - 1])
+        upd = (sig * gt)[:, None] * g.standard_normal((n, dm), dtype=np.float32)
+        H.append(bf16_round_bits(bf16_bits_to_float(H[-1]) + upd))
+    return H
