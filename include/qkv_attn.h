@@ -149,7 +149,9 @@ size_t qkv_workspace_bytes(int batch, int heads, int head_dim, int max_ctx, int 
  *            loop r stores X^(r) - Xhat^(r-1) and rebuilds Xhat^(r-1) from planes 1..r-1.
  *   pos0     multiple of 64; n_pos a positive multiple of 64; pos0 + n_pos <= cap_ctx.
  *   act_pos  device int32 [batch][ld_act]: ascending active positions of each sequence,
- *            all in [pos0, pos0+n_pos); n_act device int32 [batch] their counts.
+ *            all in [pos0, pos0+n_pos); n_act device int32 [batch] their counts
+ *            (n_act[b] <= ld_act; a list written by select_tokens, with n_before as the
+ *            counts, can be passed as it is).
  *            Both must be NULL for a dense plane (every position active).
  *   k_src, v_src  device bf16 [batch][heads][ld_src][head_dim]: row i = the i-th active
  *            position's K^(loop) / V^(loop) (post-RoPE keys).  If both are NULL the rows
@@ -222,6 +224,37 @@ int attn_decode_dense_noalloc(const qkv_cache* cache, int loop, const uint16_t* 
 int select_columns(const float* scores, int ld_scores, const float* lse, int batch, int heads,
                    int n, int k, int32_t* idx, float* p_sel, float* mass,
                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * select_tokens - the next loop's active tokens [explainer section 3, cross-loop
+ * token-sparse updates: after the dense loops, each loop ranks the tokens updated in the
+ * preceding loop by their normalized hidden-state change and keeps a top-k subset, so the
+ * active sets nest; project page STEP 01: only active tokens write new K/V].
+ *   score[t] = ||h_cur[t] - h_prev[t]||_2 / ||h_prev[t]||_2 (fp32 sums in a fixed order)
+ *   for t in the preceding active set, -inf elsewhere (a zero previous state scores +inf
+ *   for a nonzero change, 0 otherwise); the kept tokens are the top min(k, |set|) scores,
+ *   fp32 descending, ties to the lower index, written ascending.
+ *   h_cur, h_prev  device bf16 [batch][ld_tok][dm]: the preceding loop's output and input
+ *            hidden states of each token (ld_tok >= n; dm a positive multiple of 8).
+ *   act_prev, n_act_prev  device int32 [batch][ld_act] / [batch]: the preceding loop's
+ *            active tokens, ascending, each in [0, n); both NULL when every token was
+ *            active (a dense loop).  1 <= ld_act <= n.
+ *   k        1..n: tokens to keep per sequence.
+ *   split    act_out entries below this position are counted in n_before (e.g. the body
+ *            length, so that the body part can be passed to kv_encode_loop as it is).
+ *   score    device fp32 [batch][n], written.
+ *   act_out  device int32 [batch][k]: the kept tokens, ascending, in the first
+ *            n_act_out[b] entries (the rest is unspecified).
+ *   n_act_out, n_before  device int32 [batch] (n_before may be NULL).
+ *   ws       device workspace of at least qkv_token_workspace_bytes(batch, k) bytes.
+ */
+int select_tokens(const uint16_t* h_cur, const uint16_t* h_prev, int ld_tok, int batch, int n, int dm,
+                  const int32_t* act_prev, const int32_t* n_act_prev, int ld_act, int k, int split, float* score,
+                  int32_t* act_out, int32_t* n_act_out, int32_t* n_before, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* Workspace bytes select_tokens needs for `batch` sequences keeping up to k tokens. */
+size_t qkv_token_workspace_bytes(int batch, int k);
 
 /*
  * attn_decode_sparse - sparse loop `loop` (>= 2): recompute only the selected columns and

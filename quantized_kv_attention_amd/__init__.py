@@ -21,7 +21,8 @@ QKV_OK, QKV_EINVAL, QKV_EUNSUPPORTED, QKV_ECAPACITY, QKV_ELAUNCH, QKV_EWORKSPACE
 
 EXPORTED = ("qkv_strerror", "qkv_block_bytes", "qkv_body_len", "qkv_workspace_bytes", "kv_encode_loop",
             "kv_append_tail", "attn_decode_dense", "attn_decode_dense_noalloc", "select_columns",
-            "attn_decode_sparse", "qkv_export_plane", "qkv_stream_read")
+            "attn_decode_sparse", "select_tokens", "qkv_token_workspace_bytes", "qkv_export_plane",
+            "qkv_stream_read")
 NOALLOC_SCRATCH_BYTES = 4 << 20
 STREAM_READ_GROUPS = 2048
 
@@ -76,6 +77,10 @@ def lib():
     L.attn_decode_dense_noalloc.restype = i32
     L.select_columns.argtypes = [vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.select_columns.restype = i32
+    L.select_tokens.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.select_tokens.restype = i32
+    L.qkv_token_workspace_bytes.argtypes = [i32, i32]
+    L.qkv_token_workspace_bytes.restype = sz
     L.qkv_export_plane.argtypes = [cp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.qkv_export_plane.restype = i32
     L.qkv_stream_read.argtypes = [vp, sz, vp, vp]
@@ -177,6 +182,24 @@ def attn_decode_sparse(cache, loop, q, sm_scale, idx, p_sel, mass, k, o_prev, ls
                                   0 if scores is None else scores.shape[-1], _ptr(o),
                                   _ptr(o_f32), _ptr(ws), wsb, _stream(stream))
     _check("attn_decode_sparse", st)
+
+
+def token_workspace_bytes(batch, k) -> int:
+    return int(lib().qkv_token_workspace_bytes(batch, k))
+
+
+def select_tokens(h_cur, h_prev, n, k, score, act_out, n_act_out, ws, act_prev=None, n_act_prev=None, split=0,
+                  n_before=None, stream=None):
+    """The next loop's active tokens from hidden states h_cur, h_prev (bf16 [B, ld_tok, dm]):
+    top-k normalized change among act_prev (int32 [B, ld_act], n_act_prev [B]; None = every
+    token).  Writes score [B, n] fp32, act_out [B, k] int32 (ascending, n_act_out[b] valid),
+    n_act_out [B] and, if given, n_before [B] (entries below `split`)."""
+    B, ld_tok, dm = h_cur.shape
+    ld_act = 0 if act_prev is None else act_prev.shape[-1]
+    st = lib().select_tokens(_ptr(h_cur), _ptr(h_prev), ld_tok, B, n, dm, _ptr(act_prev), _ptr(n_act_prev), ld_act,
+                             k, split, _ptr(score), _ptr(act_out), _ptr(n_act_out), _ptr(n_before), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(stream))
+    _check("select_tokens", st)
 
 
 def export_plane(cache, loop, b, h, n_slots, stream=None):

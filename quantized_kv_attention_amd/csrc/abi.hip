@@ -117,7 +117,7 @@ int kv_encode_loop(const qkv_cache* cache, int loop, int pos0, int n_pos, const 
         if (act_pos || n_act) return QKV_EINVAL;
         if ((long)(pos0 + n_pos) > (long)P.n_blocks * 64) return QKV_ECAPACITY;
     } else {
-        if (!act_pos || !n_act || ld_act < n_pos) return QKV_EINVAL;
+        if (!act_pos || !n_act || ld_act < 1) return QKV_EINVAL;
     }
     if ((k_src == nullptr) != (v_src == nullptr)) return QKV_EINVAL;
     if (k_src) {
@@ -188,6 +188,25 @@ int select_columns(const float* scores, int ld_scores, const float* lse, int bat
     if (k > 0 && (!idx || !p_sel)) return QKV_EINVAL;
     if (ws_bytes < select_ws_bytes(batch, heads, n)) return QKV_EWORKSPACE;
     return launch_select(scores, ld_scores, lse, batch, heads, n, k, idx, p_sel, mass, ws, to_stream(stream));
+}
+
+int select_tokens(const uint16_t* h_cur, const uint16_t* h_prev, int ld_tok, int batch, int n, int dm,
+                  const int32_t* act_prev, const int32_t* n_act_prev, int ld_act, int k, int split, float* score,
+                  int32_t* act_out, int32_t* n_act_out, int32_t* n_before, void* ws, size_t ws_bytes, void* stream) {
+    if (!h_cur || !h_prev || !score || !act_out || !n_act_out) return QKV_EINVAL;
+    if (batch < 1 || n < 1 || dm < 8 || (dm % 8) != 0 || ld_tok < n) return QKV_EINVAL;
+    if (!aligned16(h_cur) || !aligned16(h_prev)) return QKV_EINVAL;
+    if (k < 1 || k > n) return QKV_EINVAL;
+    if ((act_prev == nullptr) != (n_act_prev == nullptr)) return QKV_EINVAL;
+    if (act_prev && (ld_act < 1 || ld_act > n)) return QKV_EINVAL;
+    if (!ws || ws_bytes < token_ws_bytes(batch, k)) return QKV_EWORKSPACE;
+    return launch_select_tokens(h_cur, h_prev, ld_tok, batch, n, dm, act_prev, n_act_prev, ld_act, k, split, score,
+                                act_out, n_act_out, n_before, ws, to_stream(stream));
+}
+
+size_t qkv_token_workspace_bytes(int batch, int k) {
+    if (batch < 1 || k < 1) return 0;
+    return (token_ws_bytes(batch, k) + 255) & ~(size_t)255;
 }
 
 int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,

@@ -42,6 +42,11 @@ int launch_select(const float* scores, int ld, const float* lse, int B, int H, i
 int launch_export_plane(const CacheArg& ca, int D, int loop, int b, int h, int n_slots, uint8_t* kc, uint8_t* vc,
                         float* ks, float* kz, float* vs, float* vz, hipStream_t st);
 
+size_t token_ws_bytes(int B, int k);
+int launch_select_tokens(const uint16_t* hc, const uint16_t* hp, int ld_tok, int B, int n, int dm,
+                         const int32_t* act, const int32_t* n_act, int ld_act, int k, int split, float* score,
+                         int32_t* act_out, int32_t* n_out, int32_t* n_before, void* ws, hipStream_t st);
+
 int launch_stream_read(const void* src, size_t n_bytes, uint32_t* sink, hipStream_t st);
 size_t sparse_ws_bytes(int B, int H, int D, int k);
 int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, const int32_t* idx,

@@ -106,6 +106,22 @@ def test_argument_validation():
     assert L.qkv_stream_read(vp(16), 40, vp(16), None) == qkv.QKV_EINVAL
     assert L.qkv_stream_read(vp(24), 64, vp(16), None) == qkv.QKV_EINVAL
     assert L.qkv_stream_read(vp(16), 64, vp(20), None) == qkv.QKV_EINVAL
+    # token selection: dm not a multiple of 8, k out of range, a list without its counts,
+    # a list longer than the context, misaligned states, short workspace
+    ws_t = qkv.token_workspace_bytes(1, 8)
+    assert ws_t >= (2 + 8) * 4
+    args = lambda **kw: dict(dict(hc=vp(16), hp=vp(16), ld=64, B=1, n=64, dm=64, ap=None, npv=None, lda=0, k=8,
+                                  ws=ws_t), **kw)
+    def tok(a):
+        return L.select_tokens(a["hc"], a["hp"], a["ld"], a["B"], a["n"], a["dm"], a["ap"], a["npv"], a["lda"],
+                               a["k"], 0, vp(16), vp(16), vp(16), None, vp(16), a["ws"], None)
+    assert tok(args(dm=60)) == qkv.QKV_EINVAL
+    assert tok(args(k=0)) == qkv.QKV_EINVAL and tok(args(k=65)) == qkv.QKV_EINVAL
+    assert tok(args(ap=vp(16))) == qkv.QKV_EINVAL
+    assert tok(args(ap=vp(16), npv=vp(16), lda=65)) == qkv.QKV_EINVAL
+    assert tok(args(hc=vp(24))) == qkv.QKV_EINVAL
+    assert tok(args(ld=32)) == qkv.QKV_EINVAL
+    assert tok(args(ws=16)) == qkv.QKV_EWORKSPACE
     # plane export: loop, sequence or head out of range, more slots than the plane holds
     assert L.qkv_export_plane(ctypes.byref(d), 3, 0, 0, 64, *[vp(16)] * 6, None) == qkv.QKV_EINVAL
     assert L.qkv_export_plane(ctypes.byref(d), 1, 1, 0, 64, *[vp(16)] * 6, None) == qkv.QKV_EINVAL
