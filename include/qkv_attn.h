@@ -123,6 +123,27 @@ typedef struct qkv_cache {
     int32_t full_state;
 } qkv_cache;
 
+/*
+ * A 64-row tail flush carried by an attention call [project page, The Method, after STEP 03:
+ * cross-loop KV updates and quantization fused into the attention kernel].  When the next
+ * decode position will move the body boundary (n_ctx - n_body == 127 in this call), the
+ * tail's 64 oldest positions [pos0, pos0 + 64), pos0 = n_body, must be encoded into every
+ * loop's plane, loops in order.  Given to loop r's attention call of the current step, the
+ * call's kernel encodes loop r's rows of that group in extra workgroups beside its readers
+ * (which do not read those positions from the planes in this step); given to every loop's
+ * call of the step, in loop order, it replaces the kv_encode_loop flush of the next step,
+ * with identical plane contents.  The caller then advances n_ctx without flushing.
+ *   pos0     must equal the body length of the current n_ctx, and pos0 + 64 <= n_ctx - 1.
+ *   act_pos, n_act, ld_act  as for kv_encode_loop: the loop's active positions among the
+ *            group (sparse planes); both NULL for a dense plane.
+ */
+typedef struct qkv_flush {
+    int32_t pos0;
+    int32_t ld_act;
+    const int32_t* act_pos;
+    const int32_t* n_act;
+} qkv_flush;
+
 /* Human-readable text of a status code (static storage). */
 const char* qkv_strerror(int status);
 
@@ -188,13 +209,16 @@ int kv_append_tail(const qkv_cache* cache, int loop, int pos0, int n_rows,
  *   scores   device fp32 [batch][heads][ld_scores]: raw logits s_j, j < n_ctx; or NULL when
  *            no later call reads them (ld_scores is then ignored).
  *   lse      device fp32 [batch][heads]: log sum_j exp(s_j).
+ *   flush    NULL, or this loop's part of the next step's tail flush (see qkv_flush).
  */
 int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,
                       const uint16_t* v_new, float sm_scale, uint16_t* o, float* o_f32, float* scores,
-                      int ld_scores, float* lse, void* ws, size_t ws_bytes, void* stream);
+                      int ld_scores, float* lse, const qkv_flush* flush, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /*
- * attn_decode_dense_noalloc - attn_decode_dense without a workspace argument, for callers
+ * attn_decode_dense_noalloc - attn_decode_dense without a workspace argument or a tail
+ * flush, for callers
  * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, outputs and kernels as
  * attn_decode_dense; the split partials go to a fixed device array inside the library,
@@ -272,12 +296,14 @@ size_t qkv_token_workspace_bytes(int batch, int k);
  *   k_new, v_new  as for attn_decode_dense: loop `loop`'s row of the newest position,
  *            stored in the loop's tail and used for that column if it is selected (its
  *            loop-(loop-1) value is read from that loop's tail, written by its own call).
+ *   flush    NULL, or this loop's part of the next step's tail flush (see qkv_flush).
  */
 int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,
                        const uint16_t* v_new, float sm_scale,
                        const int32_t* idx, const float* p_sel, const float* mass, int k,
                        const float* o_prev, const float* lse, float* scores, int ld_scores,
-                       uint16_t* o, float* o_f32, void* ws, size_t ws_bytes, void* stream);
+                       uint16_t* o, float* o_f32, const qkv_flush* flush, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /*
  * qkv_export_plane - unpacks slots [0, n_slots) of loop `loop`'s plane for sequence b, head

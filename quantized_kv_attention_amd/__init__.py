@@ -46,6 +46,11 @@ class QkvCache(ctypes.Structure):
                 ("residual_bits", ctypes.c_int32), ("full_state", ctypes.c_int32)]
 
 
+class QkvFlush(ctypes.Structure):
+    _fields_ = [("pos0", ctypes.c_int32), ("ld_act", ctypes.c_int32), ("act_pos", ctypes.c_void_p),
+                ("n_act", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -71,7 +76,8 @@ def lib():
     L.kv_encode_loop.restype = i32
     L.kv_append_tail.argtypes = [cp, i32, i32, i32, vp, vp, vp]
     L.kv_append_tail.restype = i32
-    L.attn_decode_dense.argtypes = [cp, i32, vp, vp, vp, f32, vp, vp, vp, i32, vp, vp, sz, vp]
+    fp = ctypes.POINTER(QkvFlush)
+    L.attn_decode_dense.argtypes = [cp, i32, vp, vp, vp, f32, vp, vp, vp, i32, vp, fp, vp, sz, vp]
     L.attn_decode_dense.restype = i32
     L.attn_decode_dense_noalloc.argtypes = [cp, i32, vp, vp, vp, f32, vp, vp, vp, i32, vp, vp]
     L.attn_decode_dense_noalloc.restype = i32
@@ -85,7 +91,8 @@ def lib():
     L.qkv_export_plane.restype = i32
     L.qkv_stream_read.argtypes = [vp, sz, vp, vp]
     L.qkv_stream_read.restype = i32
-    L.attn_decode_sparse.argtypes = [cp, i32, vp, vp, vp, f32, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    L.attn_decode_sparse.argtypes = [cp, i32, vp, vp, vp, f32, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, fp, vp, sz,
+                                     vp]
     L.attn_decode_sparse.restype = i32
     _lib = L
     return L
@@ -144,13 +151,19 @@ def kv_append_tail(cache, loop, pos0, k, v, stream=None):
     _check("kv_append_tail", st)
 
 
-def attn_decode_dense(cache, loop, q, sm_scale, o, o_f32, scores, lse, ws, stream=None, k_new=None, v_new=None):
+def _flush_ref(flush):
+    return None if flush is None else ctypes.byref(flush)
+
+
+def attn_decode_dense(cache, loop, q, sm_scale, o, o_f32, scores, lse, ws, stream=None, k_new=None, v_new=None,
+                      flush=None):
     """k_new / v_new: this loop's row of the newest position n_ctx - 1 ([B, H, d] bf16), stored
-    in the loop's tail by the same call; None when the tail already holds it."""
+    in the loop's tail by the same call; None when the tail already holds it.  flush: a
+    QkvFlush (this loop's part of the next step's tail flush, encoded by the same launch)."""
     st = lib().attn_decode_dense(ctypes.byref(cache.desc), loop, _ptr(q), _ptr(k_new), _ptr(v_new), float(sm_scale),
                                  _ptr(o), _ptr(o_f32),
-                                 _ptr(scores), 0 if scores is None else scores.shape[-1], _ptr(lse), _ptr(ws),
-                                 ws.numel() * ws.element_size(),
+                                 _ptr(scores), 0 if scores is None else scores.shape[-1], _ptr(lse),
+                                 _flush_ref(flush), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream))
     _check("attn_decode_dense", st)
 
@@ -173,14 +186,14 @@ def select_columns(scores, lse, n, k, idx, p_sel, mass, ws=None, stream=None):
 
 
 def attn_decode_sparse(cache, loop, q, sm_scale, idx, p_sel, mass, k, o_prev, lse, scores, o, o_f32, ws,
-                       stream=None, k_new=None, v_new=None):
-    """k_new / v_new as for attn_decode_dense."""
+                       stream=None, k_new=None, v_new=None, flush=None):
+    """k_new / v_new and flush as for attn_decode_dense."""
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     st = lib().attn_decode_sparse(ctypes.byref(cache.desc), loop, _ptr(q), _ptr(k_new), _ptr(v_new), float(sm_scale),
                                   _ptr(idx), _ptr(p_sel),
                                   _ptr(mass), k, _ptr(o_prev), _ptr(lse), _ptr(scores),
                                   0 if scores is None else scores.shape[-1], _ptr(o),
-                                  _ptr(o_f32), _ptr(ws), wsb, _stream(stream))
+                                  _ptr(o_f32), _flush_ref(flush), _ptr(ws), wsb, _stream(stream))
     _check("attn_decode_sparse", st)
 
 

@@ -13,7 +13,7 @@ import math
 import numpy as np
 import torch
 
-from . import (GROUP, MAX_LOOPS, TAIL_SLOTS, QkvCache, attn_decode_dense, attn_decode_sparse, block_bytes,
+from . import (GROUP, MAX_LOOPS, TAIL_SLOTS, QkvCache, QkvFlush, attn_decode_dense, attn_decode_sparse, block_bytes,
                body_len, kv_append_tail, kv_encode_loop, select_columns, workspace_bytes)
 
 
@@ -84,6 +84,9 @@ class LayerCache:
         self.desc = desc
         # host copy of each loop's activity for positions still in the tail
         self.act = np.zeros((n_loops, batch, cap_ctx), bool)
+        # end of the last 64-row group already encoded by attention calls (flush_args)
+        self.preflushed = 0
+        self._flush_lists = []
 
     @property
     def n_ctx(self) -> int:
@@ -174,10 +177,37 @@ class LayerCache:
         self.act[:, :, t] = True
         self.n_ctx = t + 1
 
+    def tail_full(self) -> bool:
+        """Whether the next position moves the body boundary (a 64-row flush is due)."""
+        n = self.n_ctx
+        return body_len(n + 1) > body_len(n)
+
+    def flush_args(self):
+        """Per loop, the QkvFlush of the tail's 64 oldest positions, for the attention calls
+        of the current step (each call encodes its loop's rows of the group in the same
+        launch); the next advance then does not flush them again.  Call when tail_full()."""
+        nb = body_len(self.n_ctx)
+        out, keep = [], []
+        for r in range(self.R):
+            if self.dense[r]:
+                out.append(QkvFlush(nb, 0, None, None))
+            else:
+                act_pos, n_act = self._active_lists(r, nb, nb + GROUP)
+                ap = torch.from_numpy(act_pos).to(self.device)
+                na = torch.from_numpy(n_act).to(self.device)
+                keep += [ap, na]
+                out.append(QkvFlush(nb, GROUP, ap.data_ptr(), na.data_ptr()))
+        self._flush_lists = keep   # the lists must outlive the calls that read them
+        self.preflushed = nb + GROUP
+        return out
+
     def _flush_before(self, t, stream):
         """If adding position t moves the body boundary, encodes the tail's 64 oldest
-        positions into every loop's plane, loops in order."""
+        positions into every loop's plane, loops in order (unless the attention calls of
+        the previous step have encoded them already: flush_args)."""
         nb_old, nb_new = body_len(t), body_len(t + 1)
+        if nb_new > nb_old and self.preflushed >= nb_new:
+            return
         if nb_new > nb_old:
             for r in range(self.R):
                 if self.dense[r]:
@@ -266,7 +296,7 @@ def k_columns(frac: float, n: int) -> int:
 
 
 def decode_loop(cache: LayerCache, bufs: DecodeBuffers, loop: int, q, n_dense: int, k: int, sm: float = 1.0,
-                stream=None, selected: bool = False, k_new=None, v_new=None, need_scores: bool = True):
+                stream=None, selected: bool = False, k_new=None, v_new=None, need_scores: bool = True, flush=None):
     """Attention of loop `loop` (1-based) for query q [B, H, d] bf16.
 
     A sparse loop first selects its k columns from the previous loop's scores, unless
@@ -274,12 +304,13 @@ def decode_loop(cache: LayerCache, bufs: DecodeBuffers, loop: int, q, n_dense: i
     k_new / v_new ([B, H, d] bf16): this loop's row of the newest position, stored in the
     loop's tail by the attention call itself (after LayerCache.advance_token).
     need_scores=False: the loop stores no scores (a dense loop whose next loop is dense too
-    and overwrites them; the last loop, whose scores no selection reads)."""
+    and overwrites them; the last loop, whose scores no selection reads).
+    flush: this loop's QkvFlush (LayerCache.flush_args), encoded by the same call."""
     r = loop - 1
     main = torch.cuda.current_stream() if stream is None else stream
     if loop <= n_dense:
         attn_decode_dense(cache, loop, q, sm, bufs.o[r], bufs.o_f32[r], bufs.scores if need_scores else None,
-                          bufs.lse, bufs.ws, main, k_new=k_new, v_new=v_new)
+                          bufs.lse, bufs.ws, main, k_new=k_new, v_new=v_new, flush=flush)
     else:
         assert k <= bufs.max_k
         idx, ps, mass = bufs.selection(loop, k)
@@ -287,7 +318,7 @@ def decode_loop(cache: LayerCache, bufs: DecodeBuffers, loop: int, q, n_dense: i
             select_columns(bufs.scores, bufs.lse, cache.n_ctx, k, idx, ps, mass, None, main)
         attn_decode_sparse(cache, loop, q, sm, idx, ps, mass, k, bufs.o_f32[r - 1], bufs.lse,
                            bufs.scores if need_scores else None, bufs.o[r], bufs.o_f32[r], bufs.ws, main,
-                           k_new=k_new, v_new=v_new)
+                           k_new=k_new, v_new=v_new, flush=flush)
 
 
 def scores_read_after(loop: int, n_dense: int, n_loops: int) -> bool:
@@ -296,23 +327,28 @@ def scores_read_after(loop: int, n_dense: int, n_loops: int) -> bool:
 
 
 def decode_step(cache: LayerCache, bufs: DecodeBuffers, q, n_dense: int, k: int, sm: float = 1.0, stream=None,
-                k_new=None, v_new=None):
+                k_new=None, v_new=None, fused_flush: bool = False):
     """All loops of one decode step of one layer; q[r] bf16 [B, H, d].  With k_new / v_new
     (per loop, [B, H, d] bf16) each loop's call stores its row of the newest position.  A loop
-    stores scores only when the next loop selects from them."""
+    stores scores only when the next loop selects from them.  fused_flush: when the next
+    position moves the body boundary, each loop's call also encodes its rows of the tail's
+    64 oldest positions (instead of kv_encode_loop launches at the next advance)."""
+    fl = cache.flush_args() if fused_flush and cache.tail_full() else None
     for loop in range(1, cache.R + 1):
         kn = None if k_new is None else k_new[loop - 1]
         vn = None if v_new is None else v_new[loop - 1]
         decode_loop(cache, bufs, loop, q[loop - 1], n_dense, k, sm, stream, k_new=kn, v_new=vn,
-                    need_scores=scores_read_after(loop, n_dense, cache.R))
+                    need_scores=scores_read_after(loop, n_dense, cache.R), flush=None if fl is None else fl[loop - 1])
 
 
 def decode_step_stack(stack: LayerStack, qs, n_dense: int, k: int, sm: float = 1.0, stream=None,
-                      k_new=None, v_new=None):
+                      k_new=None, v_new=None, fused_flush: bool = False):
     """One decode step of every layer of a stack, loop-major (loop r through all layers,
     then loop r+1); qs[l][r] is layer l's loop-(r+1) query.  Each sparse loop starts with
-    one selection call for all layers.  k_new[l][r] / v_new[l][r]: as for decode_step."""
+    one selection call for all layers.  k_new[l][r] / v_new[l][r] and fused_flush: as for
+    decode_step."""
     main = torch.cuda.current_stream() if stream is None else stream
+    fls = [c.flush_args() if fused_flush and c.tail_full() else None for c in stack.caches]
     for loop in range(1, stack.caches[0].R + 1):
         if loop > n_dense:
             stack.select(loop, k, main)
@@ -320,4 +356,5 @@ def decode_step_stack(stack: LayerStack, qs, n_dense: int, k: int, sm: float = 1
             kn = None if k_new is None else k_new[l][loop - 1]
             vn = None if v_new is None else v_new[l][loop - 1]
             decode_loop(c, b, loop, qs[l][loop - 1], n_dense, k, sm, main, selected=True, k_new=kn, v_new=vn,
-                        need_scores=scores_read_after(loop, n_dense, stack.caches[0].R))
+                        need_scores=scores_read_after(loop, n_dense, stack.caches[0].R),
+                        flush=None if fls[l] is None else fls[l][loop - 1])

@@ -62,6 +62,33 @@ int make_arg(const qkv_cache* c, CacheArg* a) {
 
 hipStream_t to_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Checks a tail-flush request of loop `loop` and builds its kernel argument (pos0 -1: none).
+// The group must be the tail's 64 oldest rows, and must not hold the newest position.
+int make_flush(const qkv_cache* c, int loop, const qkv_flush* f, FlushArg* out) {
+    *out = FlushArg{-1};
+    if (!f) return QKV_OK;
+    const int nb = body_len(c->n_ctx);
+    if (f->pos0 != nb || c->n_ctx < 64) return QKV_EINVAL;
+    if ((long)f->pos0 + 64 > (long)c->n_ctx - 1) return QKV_EINVAL;
+    if ((long)f->pos0 + 64 > c->cap_ctx) return QKV_ECAPACITY;
+    const qkv_plane& P = c->plane[loop - 1];
+    if (P.dense) {
+        if (f->act_pos || f->n_act) return QKV_EINVAL;
+        if ((long)f->pos0 + 64 > (long)P.n_blocks * 64) return QKV_ECAPACITY;
+    } else {
+        if (!f->act_pos || !f->n_act || f->ld_act < 1) return QKV_EINVAL;
+    }
+    out->pos0 = f->pos0;
+    out->loop = loop;
+    out->nch = c->full_state ? 0 : loop - 1;
+    out->ld_act = f->ld_act;
+    out->act_pos = P.dense ? nullptr : f->act_pos;
+    out->n_act = P.dense ? nullptr : f->n_act;
+    out->smask = P.dense ? nullptr : c->stored_loops;
+    out->bit = 1u << (loop - 1);
+    return QKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -149,7 +176,7 @@ int kv_append_tail(const qkv_cache* cache, int loop, int pos0, int n_rows, const
 
 int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,
                       const uint16_t* v_new, float sm_scale, uint16_t* o, float* o_f32, float* scores,
-                      int ld_scores, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                      int ld_scores, float* lse, const qkv_flush* flush, void* ws, size_t ws_bytes, void* stream) {
     CacheArg a;
     int st = make_arg(cache, &a);
     if (st) return st;
@@ -159,10 +186,13 @@ int attn_decode_dense(const qkv_cache* cache, int loop, const uint16_t* q, const
     if (!aligned16(q) || !aligned16(o_f32) || (o && !aligned16(o))) return QKV_EINVAL;
     if ((k_new == nullptr) != (v_new == nullptr) || (k_new && (!aligned16(k_new) || !aligned16(v_new))))
         return QKV_EINVAL;
+    FlushArg fl;
+    st = make_flush(cache, loop, flush, &fl);
+    if (st) return st;
     const size_t need = dense_ws_bytes(cache->batch, cache->heads, cache->head_dim, a.n_body);
     if (!ws || ws_bytes < need) return QKV_EWORKSPACE;
     return launch_dense(a, cache->head_dim, loop, q, NewRow{k_new, v_new}, sm_scale, o, o_f32, scores, ld_scores,
-                        lse, ws, to_stream(stream));
+                        lse, ws, to_stream(stream), fl);
 }
 
 int attn_decode_dense_noalloc(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,
@@ -212,8 +242,8 @@ size_t qkv_token_workspace_bytes(int batch, int k) {
 int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, const uint16_t* k_new,
                        const uint16_t* v_new, float sm_scale, const int32_t* idx,
                        const float* p_sel, const float* mass, int k, const float* o_prev, const float* lse,
-                       float* scores, int ld_scores, uint16_t* o, float* o_f32, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       float* scores, int ld_scores, uint16_t* o, float* o_f32, const qkv_flush* flush, void* ws,
+                       size_t ws_bytes, void* stream) {
     CacheArg a;
     int st = make_arg(cache, &a);
     if (st) return st;
@@ -224,10 +254,13 @@ int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, cons
     if (!aligned16(q) || (o && !aligned16(o))) return QKV_EINVAL;
     if ((k_new == nullptr) != (v_new == nullptr) || (k_new && (!aligned16(k_new) || !aligned16(v_new))))
         return QKV_EINVAL;
+    FlushArg fl;
+    st = make_flush(cache, loop, flush, &fl);
+    if (st) return st;
     const size_t need = sparse_ws_bytes(cache->batch, cache->heads, cache->head_dim, k);
     if (k > 0 && (!ws || ws_bytes < need)) return QKV_EWORKSPACE;
     return launch_sparse(a, cache->head_dim, loop, q, NewRow{k_new, v_new}, sm_scale, idx, p_sel, mass, k, o_prev,
-                         lse, scores, ld_scores, o, o_f32, ws, to_stream(stream));
+                         lse, scores, ld_scores, o, o_f32, ws, to_stream(stream), fl);
 }
 
 int qkv_export_plane(const qkv_cache* cache, int loop, int b, int h, int n_slots, uint8_t* k_codes,

@@ -11,6 +11,9 @@
 // the K codes of every plane into LDS logits, then a local softmax, pass 2 streams the V
 // codes; partial (max, sum, o) go to the workspace and a second kernel merges the splits
 // in a fixed order.  The last split of each (sequence, head) also reads the BF16 tail.
+#include <type_traits>
+
+#include "encode_group.h"
 #include "launch.h"
 
 namespace qkv {
@@ -106,11 +109,20 @@ __device__ __forceinline__ void vpass_block(const uint8_t* bp, int prt, int rsub
 // the last plane that stores it, so later planes overwrite logits instead of adding to
 // them, and in the V pass the deepest plane storing a position takes its probability (the
 // host passes the planes from the last dense one on, which then stores every position).
-template <int D, int NPRE, int RB, bool REPLACE>
+// FLUSH: the grid carries extra workgroups past the splits that encode this loop's 64-row
+// tail flush (FlushArg); the splits never read those rows in this launch.
+template <int D, int NPRE, int RB, bool REPLACE, bool FLUSH>
 __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                           NewRow nr, float sm, float* __restrict__ scores, int ld,
-                                                          float* __restrict__ part, int nsplit, int spb) {
+                                                          float* __restrict__ part, int nsplit, int spb,
+                                                          FlushArg fa) {
     static_assert(!REPLACE || (NPRE == 1 && RB == 4), "full-state planes: one prepared plane, 4-bit codes");
+    if constexpr (FLUSH) {
+        if ((int)blockIdx.x >= nsplit) {
+            flush_role<D, REPLACE ? 4 : RB>(ca, fa, (int)blockIdx.x - nsplit, blockIdx.y, blockIdx.z);
+            return;
+        }
+    }
     constexpr int LPR = Block<D>::kLpr, RPI = Block<D>::kRpi, NLD = 64 / RPI;
     constexpr int RBITS = REPLACE ? 4 : RB;  // code width of the planes after the first
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -558,39 +570,43 @@ CacheArg full_state_view(const CacheArg& ca, int loop, int* loop_out) {
 
 template <int D>
 static void launch_dense_d(const CacheArg& ca, int loop, const uint16_t* q, NewRow nr, float sm, uint16_t* o, float* o32,
-                           float* scores, int ld, float* lse, float* part, hipStream_t st) {
+                           float* scores, int ld, float* lse, float* part, hipStream_t st, FlushArg fl) {
     const DensePlan pl = dense_plan(ca.B, ca.H, ca.n_body);
-    dim3 grid(pl.nsplit, ca.H, ca.B);
-    if (ca.full) {
-        int lv = loop;
-        const CacheArg v = full_state_view(ca, loop, &lv);
-        dense_split_kernel<D, 1, 4, true><<<grid, 256, 0, st>>>(v, lv, q, nr, sm, scores, ld, part, pl.nsplit, pl.spb);
-    } else if (ca.rbits == 2) {
-        if (loop >= 2 && ca.p[1].dense)
-            dense_split_kernel<D, 2, 2, false><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit,
-                                                                    pl.spb);
+    int lv = loop;
+    const CacheArg v = ca.full ? full_state_view(ca, loop, &lv) : ca;
+    if (fl.pos0 >= 0) fl.loop = lv;
+    const int extra = flush_groups(fl, !ca.p[loop - 1].dense);
+    dim3 grid(pl.nsplit + extra, ca.H, ca.B);
+    const size_t dyn = extra ? (size_t)fl.nch * 64 * sizeof(int) : 0;
+    auto go = [&](auto npre, auto rb, auto rep) {
+        constexpr int NP = decltype(npre)::value, RBB = decltype(rb)::value;
+        constexpr bool RP = decltype(rep)::value;
+        if (extra)
+            dense_split_kernel<D, NP, RBB, RP, true><<<grid, 256, dyn, st>>>(v, lv, q, nr, sm, scores, ld, part,
+                                                                            pl.nsplit, pl.spb, fl);
         else
-            dense_split_kernel<D, 1, 2, false><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit,
-                                                                    pl.spb);
-    } else {
-        // plane 1 (the base) is always dense; plane 2 joins it when it is dense too
-        if (loop >= 2 && ca.p[1].dense)
-            dense_split_kernel<D, 2, 4, false><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit,
-                                                                    pl.spb);
-        else
-            dense_split_kernel<D, 1, 4, false><<<grid, 256, 0, st>>>(ca, loop, q, nr, sm, scores, ld, part, pl.nsplit,
-                                                                    pl.spb);
-    }
+            dense_split_kernel<D, NP, RBB, RP, false><<<grid, 256, 0, st>>>(v, lv, q, nr, sm, scores, ld, part,
+                                                                           pl.nsplit, pl.spb, fl);
+    };
+    using N1 = std::integral_constant<int, 1>;
+    using N2 = std::integral_constant<int, 2>;
+    using B2 = std::integral_constant<int, 2>;
+    using B4 = std::integral_constant<int, 4>;
+    // plane 1 (the base) is always dense; plane 2 joins it when it is dense too
+    const bool two = loop >= 2 && ca.p[1].dense;
+    if (ca.full) go(N1{}, B4{}, std::true_type{});
+    else if (ca.rbits == 2) { if (two) go(N2{}, B2{}, std::false_type{}); else go(N1{}, B2{}, std::false_type{}); }
+    else { if (two) go(N2{}, B4{}, std::false_type{}); else go(N1{}, B4{}, std::false_type{}); }
     dense_combine_kernel<D><<<ca.B * ca.H, 64 * kCombineWaves, 0, st>>>(part, pl.nsplit, o, o32, lse);
 }
 
 int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, uint16_t* o, float* o32,
-                 float* scores, int ld, float* lse, void* ws, hipStream_t st) {
+                 float* scores, int ld, float* lse, void* ws, hipStream_t st, FlushArg fl) {
     float* part = static_cast<float*>(ws);
     if (D == 128)
-        launch_dense_d<128>(ca, loop, q, nr, sm, o, o32, scores, ld, lse, part, st);
+        launch_dense_d<128>(ca, loop, q, nr, sm, o, o32, scores, ld, lse, part, st, fl);
     else
-        launch_dense_d<64>(ca, loop, q, nr, sm, o, o32, scores, ld, lse, part, st);
+        launch_dense_d<64>(ca, loop, q, nr, sm, o, o32, scores, ld, lse, part, st, fl);
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
 }
 

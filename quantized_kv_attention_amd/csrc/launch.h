@@ -19,6 +19,22 @@ struct NewRow {
     const uint16_t* v;
 };
 
+// The 64-row tail flush of one loop, encoded by extra workgroups of that loop's attention
+// kernel in the step before the body boundary moves: no reader of that step touches the
+// group (its positions are still tail positions), so the roles are independent.
+struct FlushArg {
+    int32_t pos0;            // first position of the group (the body length); -1: no flush
+    int32_t loop;            // the loop encoded, in the kernel argument's plane numbering
+    int32_t nch;             // planes of the chain (loop - 1; 0 for the full-state codec)
+    int32_t ld_act;
+    const int32_t* act_pos;  // sparse plane: the group's active positions, ascending; else null
+    const int32_t* n_act;
+    uint32_t* smask;         // stored-loops words kept for sparse planes, or null
+    uint32_t bit;
+};
+// extra workgroups per (head, sequence) for a flush: keys, values, and the maps of a sparse plane
+inline int flush_groups(const FlushArg& f, bool sparse_plane) { return f.pos0 < 0 ? 0 : (sparse_plane ? 3 : 2); }
+
 // split-KV plan of the dense reader: blocks per split and number of body splits
 struct DensePlan {
     int spb;
@@ -30,7 +46,7 @@ DensePlan dense_plan(int B, int H, int n_body);
 CacheArg full_state_view(const CacheArg& ca, int loop, int* loop_out);
 size_t dense_ws_bytes(int B, int H, int D, int n_body);
 int launch_dense(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, uint16_t* o, float* o32,
-                 float* scores, int ld, float* lse, void* ws, hipStream_t st);
+                 float* scores, int ld, float* lse, void* ws, hipStream_t st, FlushArg fl = FlushArg{-1});
 
 int launch_dense_noalloc(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, uint16_t* o,
                          float* o32, float* scores, int ld, float* lse, hipStream_t st);
@@ -51,6 +67,6 @@ int launch_stream_read(const void* src, size_t n_bytes, uint32_t* sink, hipStrea
 size_t sparse_ws_bytes(int B, int H, int D, int k);
 int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, const int32_t* idx,
                   const float* p_sel, const float* mass, int k, const float* o_prev, const float* lse,
-                  float* scores, int ld, uint16_t* o, float* o32, void* ws, hipStream_t st);
+                  float* scores, int ld, uint16_t* o, float* o32, void* ws, hipStream_t st, FlushArg fl = FlushArg{-1});
 
 }  // namespace qkv

@@ -20,6 +20,7 @@
 // selected scores.
 #include <type_traits>
 
+#include "encode_group.h"
 #include "launch.h"
 
 namespace qkv {
@@ -78,13 +79,21 @@ __device__ __forceinline__ void store_new_row(NewRow nr, uint16_t* tk, uint16_t*
 // RB: code width of the residual planes (planes >= 1).  REPLACE (full-state codec): a
 // column's key and value are those of the last plane storing it, not the sum of the chain
 // (the host passes the planes from the last dense one before `loop` on).
-template <int D, int SB, int RB, bool REPLACE>
+// FLUSH: extra workgroups past the chunks encode this loop's 64-row tail flush (FlushArg);
+// the chunks never read those rows' plane slots in this launch.
+template <int D, int SB, int RB, bool REPLACE, bool FLUSH>
 __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 1) void sparse_chunk_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                            NewRow nr, float sm, const int32_t* __restrict__ idx,
                                                            const float* __restrict__ p_sel, int k,
                                                            float* __restrict__ cs,
-                                                           float* __restrict__ part) {
+                                                           float* __restrict__ part, int nchunk, FlushArg fa) {
     constexpr int RBITS = REPLACE ? 4 : RB;  // code width of the planes after the first
+    if constexpr (FLUSH) {
+        if ((int)blockIdx.x >= nchunk) {
+            flush_role<D, RBITS>(ca, fa, (int)blockIdx.x - nchunk, blockIdx.y, blockIdx.z);
+            return;
+        }
+    }
     constexpr int LPC = D / 8;             // lanes per column
     constexpr int CPR = 64 / LPC;          // columns per wave round
     constexpr int ROUNDS = kWaveRounds;
@@ -96,7 +105,7 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 1) void sparse_chunk_ke
     // The newest position is the largest column, so when it is selected it is the last entry
     // of the last chunk: that workgroup stores the position's row (if given) in the tail ring
     // before any of its waves reads the tail, and no other workgroup reads that slot.
-    if (nr.k && chunk == (int)gridDim.x - 1) {
+    if (nr.k && chunk == nchunk - 1) {
         store_new_row<D>(nr, const_cast<uint16_t*>(ca.tail_k[loop - 1]), const_cast<uint16_t*>(ca.tail_v[loop - 1]),
                          b * ca.H + h, (ca.n_ctx - 1) % kTail);
         __syncthreads();
@@ -373,7 +382,7 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 1) void sparse_chunk_ke
     float M = wm[0];
 #pragma unroll
     for (int w = 1; w < kSpWaves; ++w) M = fmaxf(M, wm[w]);
-    float* out = part + ((size_t)bh * gridDim.x + chunk) * sp_record(D);
+    float* out = part + ((size_t)bh * nchunk + chunk) * sp_record(D);
     for (int t = tid; t < 2 * D; t += 64 * kSpWaves) {
         float a = 0.f;
         if (t < D) {
@@ -529,7 +538,7 @@ size_t sparse_ws_bytes(int B, int H, int D, int k) {
 
 int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, const int32_t* idx,
                   const float* p_sel, const float* mass, int k, const float* o_prev, const float* lse,
-                  float* scores, int ld, uint16_t* o, float* o32, void* ws, hipStream_t st) {
+                  float* scores, int ld, uint16_t* o, float* o32, void* ws, hipStream_t st, FlushArg fl) {
     const int nchunk = (k + chunk_cols(D) - 1) / chunk_cols(D);
     uint16_t* tk = const_cast<uint16_t*>(ca.tail_k[loop - 1]);
     uint16_t* tv = const_cast<uint16_t*>(ca.tail_v[loop - 1]);
@@ -539,7 +548,11 @@ int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow
             sparse_copy_kernel<128><<<ca.B * ca.H, 128, 0, st>>>(o_prev, o, o32, nr, tk, tv, slot);
         else
             sparse_copy_kernel<64><<<ca.B * ca.H, 64, 0, st>>>(o_prev, o, o32, nr, tk, tv, slot);
-        return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
+        if (hipGetLastError() != hipSuccess) return QKV_ELAUNCH;
+        // no chunk kernel to carry the tail flush: the encoder's own launch
+        if (fl.pos0 >= 0)
+            return launch_encode(ca, D, loop, fl.pos0, 64, fl.act_pos, fl.n_act, fl.ld_act, nullptr, nullptr, 0, st);
+        return QKV_OK;
     }
     float* part = static_cast<float*>(ws);
     float* cs = scores ? part + (size_t)ca.B * ca.H * nchunk * sp_record(D) : nullptr;  // raw scores for the splice
@@ -552,13 +565,28 @@ int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow
     // chain to hold a block
     bool batched = lv > 4;
     for (int p = 0; batched && p < lv; ++p) batched = v.p[p].data != nullptr && v.p[p].n_blocks > 0;
+    if (fl.pos0 >= 0) fl.loop = lv;
+    const int extra = flush_groups(fl, !ca.p[loop - 1].dense);
+    grid.x += extra;
+    const size_t dyn = extra ? (size_t)fl.nch * 64 * sizeof(int) : 0;
     auto chunks = [&](auto dc, auto rbc, auto fullc) {
         constexpr int DD = decltype(dc)::value, RBB = decltype(rbc)::value;
         constexpr bool FF = decltype(fullc)::value;
-        if (!batched)
-            sparse_chunk_kernel<DD, 1, RBB, FF><<<grid, 64 * kSpWaves, 0, st>>>(v, lv, q, nr, sm, idx, p_sel, k, cs, part);
-        else
-            sparse_chunk_kernel<DD, 3, RBB, FF><<<grid, 64 * kSpWaves, 0, st>>>(v, lv, q, nr, sm, idx, p_sel, k, cs, part);
+        if (!batched) {
+            if (extra)
+                sparse_chunk_kernel<DD, 1, RBB, FF, true><<<grid, 64 * kSpWaves, dyn, st>>>(v, lv, q, nr, sm, idx, p_sel,
+                                                                                        k, cs, part, nchunk, fl);
+            else
+                sparse_chunk_kernel<DD, 1, RBB, FF, false><<<grid, 64 * kSpWaves, 0, st>>>(v, lv, q, nr, sm, idx, p_sel,
+                                                                                       k, cs, part, nchunk, fl);
+        } else {
+            if (extra)
+                sparse_chunk_kernel<DD, 3, RBB, FF, true><<<grid, 64 * kSpWaves, dyn, st>>>(v, lv, q, nr, sm, idx, p_sel,
+                                                                                        k, cs, part, nchunk, fl);
+            else
+                sparse_chunk_kernel<DD, 3, RBB, FF, false><<<grid, 64 * kSpWaves, 0, st>>>(v, lv, q, nr, sm, idx, p_sel,
+                                                                                       k, cs, part, nchunk, fl);
+        }
         sparse_combine_kernel<DD><<<ca.B * ca.H, 64 * kSpCombineWaves, 0, st>>>(part, nchunk, mass, o_prev, lse, idx, cs,
                                                                               k, scores, ld, o, o32);
     };

@@ -67,7 +67,7 @@ def test_descriptor_validation(mut, expect):
     L = qkv.lib()
     d = _desc(**mut)
     vp = ctypes.c_void_p
-    st = L.attn_decode_dense(ctypes.byref(d), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None)
+    st = L.attn_decode_dense(ctypes.byref(d), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), None, vp(16), 1 << 20, None)
     assert st == expect
 
 
@@ -76,18 +76,18 @@ def test_argument_validation():
     vp = ctypes.c_void_p
     d = _desc()
     # loop out of range, null query, misaligned pointer, short workspace
-    assert L.attn_decode_dense(ctypes.byref(d), 3, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
-    assert L.attn_decode_dense(ctypes.byref(d), 1, None, None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
-    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(18), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
-    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 100, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
-    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 16, None) == qkv.QKV_EWORKSPACE
+    assert L.attn_decode_dense(ctypes.byref(d), 3, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), None, vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, None, None, None, 1.0, None, vp(16), vp(16), 256, vp(16), None, vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(18), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), None, vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 100, vp(16), None, vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), None, vp(16), 16, None) == qkv.QKV_EWORKSPACE
     # the newest position's row: both pointers or neither, 16-byte aligned
-    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), vp(16), None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
-    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), vp(16), vp(20), 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
-    assert L.attn_decode_sparse(ctypes.byref(d), 2, vp(16), None, vp(16), 1.0, vp(16), vp(16), vp(16), 4, vp(16), vp(16), vp(16), 256, None, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), vp(16), None, 1.0, None, vp(16), vp(16), 256, vp(16), None, vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(d), 1, vp(16), vp(16), vp(20), 1.0, None, vp(16), vp(16), 256, vp(16), None, vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_sparse(ctypes.byref(d), 2, vp(16), None, vp(16), 1.0, vp(16), vp(16), vp(16), 4, vp(16), vp(16), vp(16), 256, None, vp(16), None, vp(16), 1 << 20, None) == qkv.QKV_EINVAL
     # sparse loop 1 is not allowed; k beyond the context is not allowed
-    assert L.attn_decode_sparse(ctypes.byref(d), 1, vp(16), None, None, 1.0, vp(16), vp(16), vp(16), 4, vp(16), vp(16), vp(16), 256, None, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
-    assert L.attn_decode_sparse(ctypes.byref(d), 2, vp(16), None, None, 1.0, vp(16), vp(16), vp(16), 300, vp(16), vp(16), vp(16), 256, None, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_sparse(ctypes.byref(d), 1, vp(16), None, None, 1.0, vp(16), vp(16), vp(16), 4, vp(16), vp(16), vp(16), 256, None, vp(16), None, vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_sparse(ctypes.byref(d), 2, vp(16), None, None, 1.0, vp(16), vp(16), vp(16), 300, vp(16), vp(16), vp(16), 256, None, vp(16), None, vp(16), 1 << 20, None) == qkv.QKV_EINVAL
     # encode: unaligned range, dense plane with an active list, beyond capacity, tail rows not in the tail
     assert L.kv_encode_loop(ctypes.byref(d), 1, 32, 64, None, None, 0, vp(16), vp(16), 64, None) == qkv.QKV_EINVAL
     assert L.kv_encode_loop(ctypes.byref(d), 1, 0, 64, vp(16), vp(16), 64, vp(16), vp(16), 64, None) == qkv.QKV_EINVAL
@@ -122,15 +122,27 @@ def test_argument_validation():
     assert tok(args(hc=vp(24))) == qkv.QKV_EINVAL
     assert tok(args(ld=32)) == qkv.QKV_EINVAL
     assert tok(args(ws=16)) == qkv.QKV_EWORKSPACE
+    # tail flush carried by an attention call: the group must be the tail's oldest 64 rows,
+    # must not hold the newest position, and a dense plane takes no active list
+    fd = _desc(cap_ctx=320, n_ctx=300)
+    for r in range(2):
+        fd.plane[r].n_blocks = 5
+    def dflush(f):
+        return L.attn_decode_dense(ctypes.byref(fd), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 320, vp(16),
+                                   ctypes.byref(f), vp(16), 1 << 20, None)
+    assert dflush(qkv.QkvFlush(128, 0, None, None)) == qkv.QKV_EINVAL       # not the body length
+    assert dflush(qkv.QkvFlush(192, 64, 16, 16)) == qkv.QKV_EINVAL          # a dense plane with a list
+    fd.n_ctx = 256                                                            # the group holds n_ctx - 1
+    assert dflush(qkv.QkvFlush(192, 0, None, None)) == qkv.QKV_EINVAL
     # plane export: loop, sequence or head out of range, more slots than the plane holds
     assert L.qkv_export_plane(ctypes.byref(d), 3, 0, 0, 64, *[vp(16)] * 6, None) == qkv.QKV_EINVAL
     assert L.qkv_export_plane(ctypes.byref(d), 1, 1, 0, 64, *[vp(16)] * 6, None) == qkv.QKV_EINVAL
     assert L.qkv_export_plane(ctypes.byref(d), 1, 0, 1, 64, *[vp(16)] * 6, None) == qkv.QKV_EINVAL
     assert L.qkv_export_plane(ctypes.byref(d), 1, 0, 0, 257, *[vp(16)] * 6, None) == qkv.QKV_EINVAL
     # codec fields: 3-bit residuals are unsupported; the full-state codec is 4-bit only
-    assert L.attn_decode_dense(ctypes.byref(_desc(residual_bits=3)), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EUNSUPPORTED
-    assert L.attn_decode_dense(ctypes.byref(_desc(residual_bits=2, full_state=1)), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EUNSUPPORTED
-    assert L.attn_decode_dense(ctypes.byref(_desc(full_state=2)), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), vp(16), 1 << 20, None) == qkv.QKV_EINVAL
+    assert L.attn_decode_dense(ctypes.byref(_desc(residual_bits=3)), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), None, vp(16), 1 << 20, None) == qkv.QKV_EUNSUPPORTED
+    assert L.attn_decode_dense(ctypes.byref(_desc(residual_bits=2, full_state=1)), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), None, vp(16), 1 << 20, None) == qkv.QKV_EUNSUPPORTED
+    assert L.attn_decode_dense(ctypes.byref(_desc(full_state=2)), 1, vp(16), None, None, 1.0, None, vp(16), vp(16), 256, vp(16), None, vp(16), 1 << 20, None) == qkv.QKV_EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
