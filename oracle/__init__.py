@@ -65,6 +65,9 @@ def lib():
         L.orc_attend_sparse.restype = None
         L.orc_token_change.argtypes = [ctypes.c_int, ctypes.c_int, f32p, f32p, u8p, f64p]
         L.orc_token_change.restype = None
+        L.orc_prefill_sparse.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, f32p, f32p, i32p, f64p, f64p,
+                                         f32p, f32p, f32p, f32p, i32p, ctypes.c_double, f64p, f64p]
+        L.orc_prefill_sparse.restype = None
         _lib = L
     return _lib
 
@@ -220,6 +223,32 @@ def select_tokens(H_cur, H_prev, act_prev, k: int, scores_f32=None):
     kk = min(int(k), n_prev)
     idx, _, _ = select(sc, 0.0, kk)
     return idx
+
+
+# ----------------------------------------------------------------------------------
+# Prefill-side sparse loop over compact buffers (project page, The Method, after STEP 03;
+# STEP 02; explainer section 3): active query rows against one selected column set.
+# ----------------------------------------------------------------------------------
+def prefill_sparse(Q, Q0, qpos, lse0, O0, K, V, K0, V0, cpos, sm: float = 1.0):
+    """Returns (O f64 [nq, d], mass f64 [nq]); see orc_prefill_sparse."""
+    f = lambda a: np.ascontiguousarray(a, np.float32)
+    Q, Q0, K, V, K0, V0 = f(Q), f(Q0), f(K), f(V), f(K0), f(V0)
+    qpos = np.ascontiguousarray(qpos, np.int32)
+    cpos = np.ascontiguousarray(cpos, np.int32)
+    lse0 = np.ascontiguousarray(lse0, np.float64)
+    O0 = np.ascontiguousarray(O0, np.float64)
+    nq, d = Q.shape
+    nc = K.shape[0]
+    O = np.zeros((nq, d), np.float64)
+    mass = np.zeros(nq, np.float64)
+    if nc == 0:
+        K = V = K0 = V0 = np.zeros((1, d), np.float32)
+        cpos = np.zeros(1, np.int32)
+    lib().orc_prefill_sparse(nq, nc, d, _p(Q, ctypes.c_float), _p(Q0, ctypes.c_float), _p(qpos, ctypes.c_int32),
+                             _p(lse0, ctypes.c_double), _p(O0, ctypes.c_double), _p(K, ctypes.c_float),
+                             _p(V, ctypes.c_float), _p(K0, ctypes.c_float), _p(V0, ctypes.c_float),
+                             _p(cpos, ctypes.c_int32), float(sm), _p(O, ctypes.c_double), _p(mass, ctypes.c_double))
+    return O, mass
 
 
 # ----------------------------------------------------------------------------------

@@ -268,3 +268,56 @@ void orc_token_change(int n, int dm, const float* H_cur, const float* H_prev, co
         else score[t] = dd > 0.0 ? INFINITY : 0.0;
     }
 }
+
+/* ---------------------------------------------------------------------------------
+ * Prefill-side sparse loop over compact buffers [P2, The Method, after STEP 03: selected
+ * tokens and keys gathered into compact buffers so that the work stays regular GEMMs;
+ * P2 STEP 02 and P5 section 3: the rank-K correction that keeps the cached mass].
+ * Reading: during prefill a sparse loop updates its active tokens only (nq query rows at
+ * ascending positions qpos) against one set of selected columns per head (nc keys at
+ * ascending positions cpos); a row sees the columns at or before its own position (causal).
+ * For row i and its visible columns j:
+ *   s_ij  = sm q_i . K_j            (this loop's query and keys)
+ *   p_ij  = exp(sm q0_i . K0_j - lse0_i)   (the preceding loop's probability, from its
+ *                                           query, keys and log-sum-exp of row i)
+ *   m_i   = sum_j p_ij;   alpha_ij = softmax over the visible j of s_ij
+ *   o_i   = o0_i + sum_j (m_i alpha_ij V_j - p_ij V0_j)
+ * A row with no visible column keeps o0_i (m_i = 0).  fp64 throughout; inputs fp32
+ * (bf16 values held in fp32).  Shapes: Q, Q0 [nq][d]; K, V, K0, V0 [nc][d]; lse0 [nq];
+ * O0, O [nq][d]; mass [nq].
+ * ------------------------------------------------------------------------------- */
+void orc_prefill_sparse(int nq, int nc, int d, const float* Q, const float* Q0, const int32_t* qpos,
+                        const double* lse0, const double* O0, const float* K, const float* V, const float* K0,
+                        const float* V0, const int32_t* cpos, double sm, double* O, double* mass)
+{
+    double* s = (double*)malloc(sizeof(double) * (size_t)(nc > 0 ? nc : 1));
+    double* p = (double*)malloc(sizeof(double) * (size_t)(nc > 0 ? nc : 1));
+    for (int i = 0; i < nq; ++i) {
+        int nv = 0;
+        while (nv < nc && cpos[nv] <= qpos[i]) ++nv;   /* visible columns: a prefix */
+        double mx = -INFINITY, m = 0.0;
+        for (int j = 0; j < nv; ++j) {
+            double a = 0.0, b = 0.0;
+            for (int c = 0; c < d; ++c) {
+                a += (double)Q[(long)i * d + c] * (double)K[(long)j * d + c];
+                b += (double)Q0[(long)i * d + c] * (double)K0[(long)j * d + c];
+            }
+            s[j] = sm * a;
+            p[j] = exp(sm * b - lse0[i]);
+            m += p[j];
+            if (s[j] > mx) mx = s[j];
+        }
+        for (int c = 0; c < d; ++c) O[(long)i * d + c] = O0[(long)i * d + c];
+        mass[i] = m;
+        if (nv == 0) continue;
+        double l = 0.0;
+        for (int j = 0; j < nv; ++j) l += exp(s[j] - mx);
+        for (int j = 0; j < nv; ++j) {
+            double alpha = exp(s[j] - mx) / l;
+            for (int c = 0; c < d; ++c)
+                O[(long)i * d + c] += m * alpha * (double)V[(long)j * d + c] - p[j] * (double)V0[(long)j * d + c];
+        }
+    }
+    free(s);
+    free(p);
+}
