@@ -306,6 +306,47 @@ int attn_decode_sparse(const qkv_cache* cache, int loop, const uint16_t* q, cons
                        void* stream);
 
 /*
+ * kv_gather_rows - compact copies of selected rows [project page, The Method, after STEP 03:
+ * selected tokens and keys gathered into compact, compute-friendly buffers].
+ *   src      device bf16 [batch][heads][ld_src][head_dim] (head_dim 64 or 128).
+ *   idx      device int32 [batch][n_idx] (idx_per_head 0: the same rows for every head) or
+ *            [batch][heads][n_idx] (idx_per_head 1); an index outside [0, ld_src) copies zeros.
+ *   dst      transpose 0: device bf16 [batch][heads][n_idx][head_dim], row i = src row idx[i];
+ *            transpose 1: device bf16 [batch][heads][head_dim][ld_t], ld_t = n_idx rounded up
+ *            to a multiple of 32, element [c][i] = src[idx[i]][c], zero for i >= n_idx
+ *            (the value layout attn_prefill_sparse takes).
+ */
+int kv_gather_rows(const uint16_t* src, int batch, int heads, int ld_src, int head_dim, const int32_t* idx, int n_idx,
+                   int idx_per_head, int transpose, uint16_t* dst, void* stream);
+
+/*
+ * attn_prefill_sparse - prefill-side sparse loop r over compact buffers [project page, The
+ * Method, after STEP 03: selected tokens and keys in compact buffers, regular GEMMs; STEP 02
+ * and explainer section 3: the rank-K correction of loop r-1's output that keeps the cached
+ * mass].  For each active query row i and the selected columns j at or before its position:
+ *   p_ij = exp(sm q_prev_i . k_prev_j - lse_prev_i),  m_i = sum_j p_ij,
+ *   alpha_ij = softmax_j(sm q_i . k_j),
+ *   o_i = o_prev_i + sum_j (m_i alpha_ij v_j - p_ij v_prev_j)   (no column: o_prev_i).
+ * bf16 MFMA products with fp32 accumulation.
+ *   q, q_prev   device bf16 [batch][heads][n_q][head_dim]: loop r's and loop r-1's queries of
+ *               the active tokens (kv_gather_rows of the full query rows).
+ *   q_pos       device int32 [batch][n_q]: the active tokens' positions, ascending.
+ *   lse_prev    device fp32 [batch][heads][n_q]: loop r-1's log-sum-exp of each active row.
+ *   o_prev      device fp32 [batch][heads][n_q][head_dim]: loop r-1's output of those rows.
+ *   k, k_prev   device bf16 [batch][heads][n_c][head_dim]: the selected columns' keys.
+ *   v_t, v_prev_t  device bf16 [batch][heads][head_dim][ld_t]: their values, transposed
+ *               (kv_gather_rows with transpose 1; ld_t = n_c rounded up to 32, zero-filled).
+ *   c_pos       device int32 [batch][heads][n_c]: the selected columns' positions, ascending.
+ *   n_c         0..: selected columns per head (0: o = o_prev).
+ *   o_f32       device fp32 [batch][heads][n_q][head_dim]; o (bf16, same shape) may be NULL;
+ *   mass        device fp32 [batch][heads][n_q] (m_i) or NULL.
+ */
+int attn_prefill_sparse(int batch, int heads, int head_dim, const uint16_t* q, const uint16_t* q_prev,
+                        const int32_t* q_pos, int n_q, const float* lse_prev, const float* o_prev, const uint16_t* k,
+                        const uint16_t* k_prev, const uint16_t* v_t, const uint16_t* v_prev_t, const int32_t* c_pos,
+                        int n_c, float sm_scale, float* o_f32, uint16_t* o, float* mass, void* stream);
+
+/*
  * qkv_export_plane - unpacks slots [0, n_slots) of loop `loop`'s plane for sequence b, head
  * h into plain arrays, so that a test can compare a plane's logical content with a
  * reference without decoding the packed layout above (test and inspection use; not on

@@ -21,8 +21,8 @@ QKV_OK, QKV_EINVAL, QKV_EUNSUPPORTED, QKV_ECAPACITY, QKV_ELAUNCH, QKV_EWORKSPACE
 
 EXPORTED = ("qkv_strerror", "qkv_block_bytes", "qkv_body_len", "qkv_workspace_bytes", "kv_encode_loop",
             "kv_append_tail", "attn_decode_dense", "attn_decode_dense_noalloc", "select_columns",
-            "attn_decode_sparse", "select_tokens", "qkv_token_workspace_bytes", "qkv_export_plane",
-            "qkv_stream_read")
+            "attn_decode_sparse", "select_tokens", "qkv_token_workspace_bytes", "kv_gather_rows",
+            "attn_prefill_sparse", "qkv_export_plane", "qkv_stream_read")
 NOALLOC_SCRATCH_BYTES = 4 << 20
 STREAM_READ_GROUPS = 2048
 
@@ -87,6 +87,11 @@ def lib():
     L.select_tokens.restype = i32
     L.qkv_token_workspace_bytes.argtypes = [i32, i32]
     L.qkv_token_workspace_bytes.restype = sz
+    L.kv_gather_rows.argtypes = [vp, i32, i32, i32, i32, vp, i32, i32, i32, vp, vp]
+    L.kv_gather_rows.restype = i32
+    L.attn_prefill_sparse.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp,
+                                      vp]
+    L.attn_prefill_sparse.restype = i32
     L.qkv_export_plane.argtypes = [cp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.qkv_export_plane.restype = i32
     L.qkv_stream_read.argtypes = [vp, sz, vp, vp]
@@ -213,6 +218,32 @@ def select_tokens(h_cur, h_prev, n, k, score, act_out, n_act_out, ws, act_prev=N
                              k, split, _ptr(score), _ptr(act_out), _ptr(n_act_out), _ptr(n_before), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream))
     _check("select_tokens", st)
+
+
+def gather_rows(src, idx, transpose=False, stream=None):
+    """Compact rows of src (bf16 [B, H, ld_src, d]) at idx (int32 [B, n] shared by the heads, or
+    [B, H, n]): [B, H, n, d], or transposed [B, H, d, ld_t] with ld_t = n rounded up to 32."""
+    import torch
+    B, H, ld, d = src.shape
+    per_head = 1 if idx.dim() == 3 else 0
+    n = idx.shape[-1]
+    ldt = ((n + 31) // 32) * 32
+    dst = torch.empty((B, H, d, ldt) if transpose else (B, H, n, d), dtype=src.dtype, device=src.device)
+    st = lib().kv_gather_rows(_ptr(src), B, H, ld, d, _ptr(idx), n, per_head, 1 if transpose else 0, _ptr(dst),
+                              _stream(stream))
+    _check("kv_gather_rows", st)
+    return dst
+
+
+def attn_prefill_sparse(q, q_prev, q_pos, lse_prev, o_prev, k, k_prev, v_t, v_prev_t, c_pos, sm_scale, o_f32, o=None,
+                        mass=None, stream=None):
+    """Prefill-side sparse loop over compact buffers (see include/qkv_attn.h)."""
+    B, H, n_q, d = q.shape
+    n_c = k.shape[2]
+    st = lib().attn_prefill_sparse(B, H, d, _ptr(q), _ptr(q_prev), _ptr(q_pos), n_q, _ptr(lse_prev), _ptr(o_prev),
+                                   _ptr(k), _ptr(k_prev), _ptr(v_t), _ptr(v_prev_t), _ptr(c_pos), n_c,
+                                   float(sm_scale), _ptr(o_f32), _ptr(o), _ptr(mass), _stream(stream))
+    _check("attn_prefill_sparse", st)
 
 
 def export_plane(cache, loop, b, h, n_slots, stream=None):

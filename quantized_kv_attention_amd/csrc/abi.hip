@@ -276,6 +276,32 @@ int qkv_export_plane(const qkv_cache* cache, int loop, int b, int h, int n_slots
                                v_zero, to_stream(stream));
 }
 
+int kv_gather_rows(const uint16_t* src, int batch, int heads, int ld_src, int head_dim, const int32_t* idx, int n_idx,
+                   int idx_per_head, int transpose, uint16_t* dst, void* stream) {
+    if (!src || !idx || !dst || batch < 1 || heads < 1 || ld_src < 1 || n_idx < 1) return QKV_EINVAL;
+    if (head_dim != 64 && head_dim != 128) return QKV_EUNSUPPORTED;
+    if ((idx_per_head != 0 && idx_per_head != 1) || (transpose != 0 && transpose != 1)) return QKV_EINVAL;
+    if (!aligned16(src) || !aligned16(dst)) return QKV_EINVAL;
+    return launch_gather_rows(src, batch, heads, ld_src, head_dim, idx, n_idx, idx_per_head, transpose, dst,
+                              to_stream(stream));
+}
+
+int attn_prefill_sparse(int batch, int heads, int head_dim, const uint16_t* q, const uint16_t* q_prev,
+                        const int32_t* q_pos, int n_q, const float* lse_prev, const float* o_prev, const uint16_t* k,
+                        const uint16_t* k_prev, const uint16_t* v_t, const uint16_t* v_prev_t, const int32_t* c_pos,
+                        int n_c, float sm_scale, float* o_f32, uint16_t* o, float* mass, void* stream) {
+    if (batch < 1 || heads < 1 || n_q < 1 || n_c < 0) return QKV_EINVAL;
+    if (head_dim != 64 && head_dim != 128) return QKV_EUNSUPPORTED;
+    if (!q || !q_prev || !q_pos || !lse_prev || !o_prev || !o_f32) return QKV_EINVAL;
+    if (n_c > 0 && (!k || !k_prev || !v_t || !v_prev_t || !c_pos)) return QKV_EINVAL;
+    if (!aligned16(q) || !aligned16(q_prev) || !aligned16(o_prev) || !aligned16(o_f32) || (o && !aligned16(o)))
+        return QKV_EINVAL;
+    if (n_c > 0 && (!aligned16(k) || !aligned16(k_prev) || !aligned16(v_t) || !aligned16(v_prev_t)))
+        return QKV_EINVAL;
+    return launch_prefill_sparse(batch, heads, head_dim, q, q_prev, q_pos, n_q, lse_prev, o_prev, k, k_prev, v_t,
+                                 v_prev_t, c_pos, n_c, sm_scale, o_f32, o, mass, to_stream(stream));
+}
+
 int qkv_stream_read(const void* src, size_t n_bytes, uint32_t* sink, void* stream) {
     if (!src || !sink || n_bytes == 0 || (n_bytes % 16) != 0 || !aligned16(src) || !aligned16(sink))
         return QKV_EINVAL;

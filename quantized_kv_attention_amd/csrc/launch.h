@@ -63,6 +63,13 @@ int launch_select_tokens(const uint16_t* hc, const uint16_t* hp, int ld_tok, int
                          const int32_t* act, const int32_t* n_act, int ld_act, int k, int split, float* score,
                          int32_t* act_out, int32_t* n_out, int32_t* n_before, void* ws, hipStream_t st);
 
+int launch_gather_rows(const uint16_t* src, int B, int H, int ld_src, int D, const int32_t* idx, int n, int per_head,
+                       int transpose, uint16_t* dst, hipStream_t st);
+int launch_prefill_sparse(int B, int H, int D, const uint16_t* q1, const uint16_t* q0, const int32_t* qpos, int n_q,
+                          const float* lse0, const float* o0, const uint16_t* k1, const uint16_t* k0,
+                          const uint16_t* v1t, const uint16_t* v0t, const int32_t* cpos, int n_c, float sm,
+                          float* o32, uint16_t* o16, float* mass, hipStream_t st);
+
 int launch_stream_read(const void* src, size_t n_bytes, uint32_t* sink, hipStream_t st);
 size_t sparse_ws_bytes(int B, int H, int D, int k);
 int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, const int32_t* idx,

@@ -25,7 +25,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-KIND_KV, KIND_MASK, KIND_Q, KIND_NEW, KIND_HIDDEN = 1, 2, 3, 4, 5
+KIND_KV, KIND_MASK, KIND_Q, KIND_NEW, KIND_HIDDEN, KIND_PREFILL_Q, KIND_COLS = 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclass
@@ -238,3 +238,22 @@ def gen_hidden(w: Workload, dm: int, n: int | None = None, b: int = 0):
         upd = (sig * gt)[:, None] * g.standard_normal((n, dm), dtype=np.float32)
         H.append(bf16_round_bits(bf16_bits_to_float(H[-1]) + upd))
     return H
+
+
+def gen_prefill_queries(w: Workload, b: int, h: int, n: int | None = None):
+    """Per-loop queries of every prompt token of one (sequence, head) for prefill: Q[r]
+    uint16 (bf16 bits) [n, d]; q^(1) ~ N(0,1)/sqrt(d), q^(r) = bf16(q^(r-1) + sigma_r N(0,1)/sqrt(d))."""
+    n = w.n if n is None else n
+    g = _rng(w.seed, KIND_PREFILL_Q, b, h)
+    sd = np.float32(1.0 / math.sqrt(w.d))
+    Q = [bf16_round_bits(g.standard_normal((n, w.d), dtype=np.float32) * sd)]
+    for r in range(1, w.R):
+        sig = np.float32(w.sigma[r - 1])
+        Q.append(bf16_round_bits(bf16_bits_to_float(Q[-1]) + sig * sd * g.standard_normal((n, w.d), dtype=np.float32)))
+    return Q
+
+
+def gen_columns(w: Workload, n: int, k: int, b: int, h: int):
+    """A selected column set of one (sequence, head): k positions of [0, n), ascending."""
+    g = _rng(w.seed, KIND_COLS, b, h)
+    return np.sort(g.choice(n, size=min(k, n), replace=False)).astype(np.int32)
