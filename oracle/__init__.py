@@ -68,6 +68,9 @@ def lib():
         L.orc_prefill_sparse.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, f32p, f32p, i32p, f64p, f64p,
                                          f32p, f32p, f32p, f32p, i32p, ctypes.c_double, f64p, f64p]
         L.orc_prefill_sparse.restype = None
+        L.orc_rebuild_plane.argtypes = [ctypes.c_int, ctypes.c_int, i32p, u8p, f32p, f32p, u8p, f32p, f32p,
+                                        ctypes.c_int, f32p, f32p]
+        L.orc_rebuild_plane.restype = None
         _lib = L
     return _lib
 
@@ -383,8 +386,42 @@ class OracleCache:
         self.n = t + 1
         self._set_tail(t, t + 1)
 
+    # -- reconstruction from the stored planes (the chain dequantisation of a decode step) --
+    def rebuild(self, b: int, h: int):
+        """Per loop, K and V reconstructions [n, d] of (b, h) rebuilt from the stored plane
+        records alone (the loop's BF16 tail rows for tail positions), as a reader of the
+        stored cache does each step: base plus residuals, or the last plane storing a
+        position in the full-state codec."""
+        n, d = self.n, self.d
+        Ks, Vs = [], []
+        Kx = np.zeros((self.cap, d), np.float32)
+        Vx = np.zeros((self.cap, d), np.float32)
+        for r in range(self.R):
+            rec = self.planes[b][h][r]
+            ns = rec.pos.size
+            if ns:
+                first = 1 if (r == 0 or self.full_state) else 0
+                if first and r > 0:
+                    Kx, Vx = Kx.copy(), Vx.copy()   # positions the plane does not store keep loop r-1
+                lib().orc_rebuild_plane(ns, d, _p(rec.pos, ctypes.c_int32), _p(np.ascontiguousarray(rec.kc), ctypes.c_uint8),
+                                        _p(np.ascontiguousarray(rec.ks), ctypes.c_float),
+                                        _p(np.ascontiguousarray(rec.kz), ctypes.c_float),
+                                        _p(np.ascontiguousarray(rec.vc), ctypes.c_uint8),
+                                        _p(np.ascontiguousarray(rec.vs), ctypes.c_float),
+                                        _p(np.ascontiguousarray(rec.vz), ctypes.c_float), first,
+                                        _p(Kx, ctypes.c_float), _p(Vx, ctypes.c_float))
+            Kr, Vr = Kx[:n].copy(), Vx[:n].copy()
+            # tail rows: the loop's BF16 values (an inactive token holds loop r-1's)
+            Kr[self.nb:n] = self.Khat[r][b, h, self.nb:n]
+            Vr[self.nb:n] = self.Vhat[r][b, h, self.nb:n]
+            Ks.append(Kr)
+            Vs.append(Vr)
+            Kx, Vx = Kx.copy(), Vx.copy()
+        return Ks, Vs
+
     # -- one decode step over all loops (PyPI Configuration: dense loops, then sparse) --
-    def step(self, q, n_dense: int, k: int, sm: float = 1.0, threads: int = 1, teacher=None):
+    def step(self, q, n_dense: int, k: int, sm: float = 1.0, threads: int = 1, teacher=None,
+             from_planes: bool = False):
         """Runs loops 1..R for query q[r] (uint16 bf16 bits [B,H,d]).
 
         Loops 1..n_dense are dense; later loops select k columns from the scores left by
@@ -394,7 +431,9 @@ class OracleCache:
         splice on identical inputs).
 
         Returns a list over loops of dicts with o (f64 [B,H,d]), scores (f64 [B,H,n]),
-        lse (f64 [B,H]) and, for sparse loops, idx/p_sel/mass.
+        lse (f64 [B,H]) and, for sparse loops, idx/p_sel/mass.  from_planes: every head first
+        rebuilds its reconstructions from the stored planes (rebuild), as a reader of the
+        stored cache does, instead of taking the ones kept at encode time (same values).
         """
         B, H, d, n = self.B, self.H, self.d, self.n
         out = []
@@ -404,10 +443,12 @@ class OracleCache:
             b, h = bh
             res = []
             scores = lse = o_prev = None
+            if from_planes:
+                KK, VV = self.rebuild(b, h)
             for r in range(self.R):
                 qf = bf16_bits_to_f32(q[r][b, h])
-                Kr = self.Khat[r][b, h, :n]
-                Vr = self.Vhat[r][b, h, :n]
+                Kr = KK[r] if from_planes else self.Khat[r][b, h, :n]
+                Vr = VV[r] if from_planes else self.Vhat[r][b, h, :n]
                 if r < n_dense:
                     o, scores, lse = attend_dense(qf, Kr, Vr, sm)
                     res.append(dict(o=o, scores=scores.copy(), lse=lse))
@@ -423,8 +464,8 @@ class OracleCache:
                         o_in = o_prev
                         sc_in = scores
                     idx, p_sel, mass = select(sel_scores, sel_lse, k)
-                    o, scores = attend_sparse(qf, Kr, Vr, self.Vhat[r - 1][b, h, :n], idx, p_sel, mass,
-                                              o_in, sel_lse, sc_in, sm)
+                    Vprev = VV[r - 1] if from_planes else self.Vhat[r - 1][b, h, :n]
+                    o, scores = attend_sparse(qf, Kr, Vr, Vprev, idx, p_sel, mass, o_in, sel_lse, sc_in, sm)
                     lse = sel_lse
                     res.append(dict(o=o, scores=scores.copy(), lse=lse, idx=idx, p_sel=p_sel, mass=mass))
                 o_prev = o

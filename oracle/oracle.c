@@ -321,3 +321,29 @@ void orc_prefill_sparse(int nq, int nc, int d, const float* Q, const float* Q0, 
     free(s);
     free(p);
 }
+
+/* ---------------------------------------------------------------------------------
+ * Rebuild of one loop's reconstruction from its stored plane [P2 STEP 03; P5 section 3]:
+ * for every stored slot s (position pos[s] >= 0) of loop r's plane, the dequantised codes
+ * are added to the previous loop's reconstruction (first = 1: loop 1, the base, or every
+ * loop of the full-state codec, where they replace it).  K groups are 64 consecutive slots
+ * (metadata per group), V groups 64 consecutive channels (metadata per slot).
+ *   X[cap][d] holds loop r-1's reconstruction on entry (any value if first) and loop r's on
+ *   exit for the stored positions; other positions are left as they are.
+ * ------------------------------------------------------------------------------- */
+void orc_rebuild_plane(int nslots, int d, const int32_t* pos, const uint8_t* kc, const float* ks, const float* kz,
+                       const uint8_t* vc, const float* vs, const float* vz, int first, float* Kx, float* Vx)
+{
+    int gpr = d / ORC_GROUP;
+    for (int s = 0; s < nslots; ++s) {
+        long p = pos[s];
+        if (p < 0) continue;
+        int g = s / ORC_GROUP;
+        for (int c = 0; c < d; ++c) {
+            float dk = orc_dequant(kc[(long)s * d + c], ks[(long)g * d + c], kz[(long)g * d + c]);
+            float dv = orc_dequant(vc[(long)s * d + c], vs[(long)s * gpr + c / ORC_GROUP], vz[(long)s * gpr + c / ORC_GROUP]);
+            Kx[p * d + c] = first ? dk : Kx[p * d + c] + dk;
+            Vx[p * d + c] = first ? dv : Vx[p * d + c] + dv;
+        }
+    }
+}

@@ -117,3 +117,27 @@ def test_step_all_columns_equals_dense(tiny_cache):
         assert part[r]["idx"][0][0].size == w.k_cols()
         diff = np.abs(part[r]["o"] - dense[r]["o"]).max()
         assert 0 < diff < 0.5
+
+
+@pytest.mark.parametrize("codec", [{}, dict(residual_bits=2), dict(full_state=True)],
+                         ids=["int4-residual", "int2-residual", "full-state"])
+def test_rebuild_from_planes_equals_encode_time_reconstruction(orc, codec):
+    # two paths of the oracle: the reconstruction kept while encoding (quantizer output) and
+    # the dequantisation of the stored codes alone must agree bit for bit, also after a flush
+    from quantized_kv_attention_amd import synth
+    w = synth.WORKLOADS["tiny"]
+    K, V, act = synth.gen_layer(w, n=700)
+    oc = orc.OracleCache(w.B, w.H, w.d, w.R, 832, **codec)
+    oc.prefill(K, V, act)
+    for step in range(70):
+        k, v = synth.gen_new_token(w, step)
+        oc.append(k, v)
+    Ks, Vs = oc.rebuild(0, 0)
+    for r in range(w.R):
+        assert np.array_equal(Ks[r].view(np.uint32), oc.Khat[r][0, 0, :oc.n].view(np.uint32)), f"K loop {r + 1}"
+        assert np.array_equal(Vs[r].view(np.uint32), oc.Vhat[r][0, 0, :oc.n].view(np.uint32)), f"V loop {r + 1}"
+    q = synth.gen_queries(w, 3)
+    a = oc.step(q, w.n_dense, w.k_cols(oc.n))
+    bb = oc.step(q, w.n_dense, w.k_cols(oc.n), from_planes=True)
+    for r in range(w.R):
+        assert np.array_equal(a[r]["o"], bb[r]["o"])
