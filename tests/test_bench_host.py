@@ -23,10 +23,17 @@ def _summary(path, source_hash, hbm):
 
 
 def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
-    p = tmp_path / "traffic.txt"
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
-    assert bench.read_traffic() is None                       # no summary
-    _summary(p, bench._dense_source_hash(), 171000000)
-    assert bench.read_traffic() == 171000000                  # taken on this source
-    _summary(p, "0" * 16, 171000000)
-    assert bench.read_traffic() is None                       # taken on another source
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    for key, (fname, _, srcs) in bench.TRAFFIC.items():
+        p = tmp_path / "profiles" / fname
+        assert bench.read_traffic(key) is None                  # no summary
+        _summary(p, bench.source_hash(srcs), 171000000)
+        assert bench.read_traffic(key) == 171000000             # taken on this source
+        _summary(p, "0" * 16, 171000000)
+        assert bench.read_traffic(key) is None                  # taken on another source
+
+
+def test_cpu_info_names_the_host():
+    model, nproc = bench.cpu_info()
+    assert nproc >= 1 and isinstance(model, str)

@@ -33,3 +33,13 @@ def test_plane_bytes():
     # 64 rows x d=128: 8 KiB codes + 1 KiB key metadata + 1 KiB value metadata = one block
     assert bm.plane_bytes(64, 128) == 10240
     assert bm.plane_bytes(65, 128) == 65 * 128 + 2 * 1024 + 65 * 16
+
+
+def test_plane_bytes_two_bit_and_prefill_flops():
+    # 2-bit codes take half the code bytes, the metadata stays
+    assert bm.plane_bytes(64, 128, 2) == 64 * 128 // 2 + 1024 + 1024
+    # one row at position 10 sees the columns at 3 and 10, not 11: 2 pairs x 4 products x 2 d
+    assert bm.prefill_sparse_flops([10], [3, 10, 11], 64) == 2 * 4 * 2 * 64
+    # the full-state encode re-reads no chain
+    assert bm.encode_bytes(64, 128, 3, full_state=True) == 64 * 128 * 4 + 10240
+    assert bm.encode_bytes(64, 128, 3) == 64 * 128 * 4 + 3 * 10240
