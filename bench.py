@@ -439,9 +439,9 @@ def rooflines(rows, loop_bytes, w, rot):
     entry("sparse4", "sparse_chunk_kernel<128,1> + sparse_combine_kernel<128> (loop 4)", s4["us"], s4["bytes"],
           s4["us"])
     sel = [v for k_, v in rows.items() if k_.startswith("select_columns") and "layers per call" in k_]
-    if sel:
-        e = entry("select", f"select_kernel ({rot.L} layers per call, per layer)", sel[0]["us"], sel[0]["bytes"],
-                  sum(v["us"] for v in sel))
+    if sel:   # one launch selects for every rotated layer
+        e = entry("select", f"select_kernel (one launch for {rot.L} layers)", sel[0]["us"] * rot.L,
+                  sel[0]["bytes"] * rot.L, sum(v["us"] for v in sel))
         e["bound"] = "latency"
     # the step's largest share: the sparse gather runs twice (loops 3 and 4)
     fams = {"dense_split_kernel<128,2> (loop 2)": (d2["us"], d2["bytes"], "dense2", d2["us"]),

@@ -121,7 +121,15 @@ typedef struct qkv_cache {
      *                  loop <= r that stores it (requires residual_bits 4). */
     int32_t residual_bits;
     int32_t full_state;
+    /* NULL, or a device uint32 the caller zeroes: kv_encode_loop (and a flush carried by an
+     * attention call) sets bit 0 (QKV_FLAG_PLANE_FULL) when a sparse plane has no block left
+     * for a group of active rows; those rows are then not stored, and later reads of those
+     * positions use the previous loop's values.  Size sparse planes with n_blocks >= the
+     * active rows / 64 plus one block per encode call, or check this word. */
+    uint32_t* error_flags;
 } qkv_cache;
+
+#define QKV_FLAG_PLANE_FULL 1u
 
 /*
  * A 64-row tail flush carried by an attention call [project page, The Method, after STEP 03:

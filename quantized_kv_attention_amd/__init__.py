@@ -24,6 +24,7 @@ EXPORTED = ("qkv_strerror", "qkv_block_bytes", "qkv_body_len", "qkv_workspace_by
             "attn_decode_sparse", "select_tokens", "qkv_token_workspace_bytes", "kv_gather_rows",
             "attn_prefill_sparse", "qkv_export_plane", "qkv_stream_read")
 NOALLOC_SCRATCH_BYTES = 4 << 20
+FLAG_PLANE_FULL = 1
 STREAM_READ_GROUPS = 2048
 
 
@@ -43,7 +44,8 @@ class QkvCache(ctypes.Structure):
                 ("n_loops", ctypes.c_int32), ("cap_ctx", ctypes.c_int32), ("n_ctx", ctypes.c_int32),
                 ("plane", QkvPlane * MAX_LOOPS), ("tail_k", ctypes.c_void_p * MAX_LOOPS),
                 ("tail_v", ctypes.c_void_p * MAX_LOOPS), ("stored_loops", ctypes.c_void_p),
-                ("residual_bits", ctypes.c_int32), ("full_state", ctypes.c_int32)]
+                ("residual_bits", ctypes.c_int32), ("full_state", ctypes.c_int32),
+                ("error_flags", ctypes.c_void_p)]
 
 
 class QkvFlush(ctypes.Structure):

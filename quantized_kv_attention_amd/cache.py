@@ -81,12 +81,20 @@ class LayerCache:
         # over a deep chain skip the planes that do not store a column)
         self.stored_loops = torch.zeros((batch, cap_ctx), dtype=torch.int32, device=device)
         desc.stored_loops = self.stored_loops.data_ptr()
+        # error word of the encoder (a sparse plane without room for a group of active rows)
+        self.error_flags = torch.zeros(1, dtype=torch.int32, device=device)
+        desc.error_flags = self.error_flags.data_ptr()
         self.desc = desc
         # host copy of each loop's activity for positions still in the tail
         self.act = np.zeros((n_loops, batch, cap_ctx), bool)
         # end of the last 64-row group already encoded by attention calls (flush_args)
         self.preflushed = 0
         self._flush_lists = []
+
+    def errors(self) -> int:
+        """The encoder's error word (FLAG_PLANE_FULL: rows of a full sparse plane were not
+        stored); synchronizes with the device."""
+        return int(self.error_flags.item())
 
     @property
     def n_ctx(self) -> int:

@@ -32,6 +32,7 @@ int make_arg(const qkv_cache* c, CacheArg* a) {
     a->full = c->full_state;
     if (c->stored_loops && !aligned16(c->stored_loops)) return QKV_EINVAL;
     a->smask = c->stored_loops;
+    a->eflags = c->error_flags;
     for (int p = 0; p < QKV_MAX_LOOPS; ++p) {
         PlaneArg& P = a->p[p];
         P = PlaneArg{};

@@ -67,6 +67,7 @@ struct CacheArg {
     const uint16_t* tail_k[QKV_MAX_LOOPS];
     const uint16_t* tail_v[QKV_MAX_LOOPS];
     uint32_t* smask;   // [B][cap_ctx]: bit p set iff sparse plane p stores the position, or null
+    uint32_t* eflags;  // error word (QKV_FLAG_PLANE_FULL), or null
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t u16) { return __uint_as_float(u16 << 16); }

@@ -74,7 +74,10 @@ __device__ __forceinline__ void encode_group(const CacheArg& ca, int loop, int n
     const int nstart = ca.cap_ctx / 64 + 1;
     const int base = dense ? pos0 : P.rowstart[(size_t)b * nstart + pos0 / 64];
     const int blk_idx = (base + r0) >> 6;
-    if (blk_idx >= P.n_blocks) return;  // sparse plane full: rows beyond its capacity are not stored
+    if (blk_idx >= P.n_blocks) {  // sparse plane full: the rows are not stored, and the caller is told
+        if (tid == 0 && ca.eflags) atomicOr(ca.eflags, QKV_FLAG_PLANE_FULL);
+        return;
+    }
     uint8_t* blk = const_cast<uint8_t*>(block_ptr<D, OUTB>(P, ca.H, b, h, blk_idx));
     const bool from_tail = (ksrc == nullptr);
     const size_t bh = (size_t)b * ca.H + h;

@@ -210,3 +210,17 @@ def test_sparse_loop_without_scores():
     torch.cuda.synchronize()
     assert torch.equal(b.o[r], ref[0]) and torch.equal(b.o_f32[r], ref[1])
     assert torch.equal(b.scores, saved)
+
+
+def test_full_sparse_plane_is_reported():
+    # loop 3 keeps 25% of 1000 positions (4 groups of rows) but its plane holds 2 blocks: the
+    # encoder stores what fits and sets the error word; a plane with room leaves it 0
+    import math
+
+    import quantized_kv_attention_amd as qkv
+    w = dataclasses.replace(W["ctx4k"], H=2)
+    K, V, act = synth.gen_layer(w, n=1000)
+    for blocks, expect in ((2, qkv.FLAG_PLANE_FULL), (6, 0)):
+        c = qcache.LayerCache(w.B, w.H, w.d, w.R, 1088, sparse_blocks=[0, 0, blocks, blocks])
+        c.prefill([to_dev_bf16(k) for k in K], [to_dev_bf16(v) for v in V], act)
+        assert c.errors() == expect, (blocks, c.errors())
