@@ -45,17 +45,38 @@ __device__ __forceinline__ float row_sum4(float v) { return add_xor32(add_xor16(
 constexpr int kPfRows = 64;   // query rows per workgroup (16 per wave)
 constexpr int kPfCols = 32;   // columns per step (two 16-column blocks)
 
+// LDS tiles of one step, shared by the workgroup's four waves: key rows of both loops
+// ([column][channel], rows padded by 16 bytes so that the 16 lanes reading 16 columns at one
+// channel offset fall into distinct banks) and transposed values of both loops ([channel]
+// [column], rows of 32 columns padded to 72 bytes for the same reason).
 template <int D>
-__global__ __launch_bounds__(256) void prefill_sparse_kernel(
+struct PfTile {
+    static constexpr int kKRow = D * 2 + 16;
+    static constexpr int kVRow = kPfCols * 2 + 8;
+    static constexpr int kK = kPfCols * kKRow;       // one key tile
+    static constexpr int kV = D * kVRow;             // one value tile
+    static constexpr int kPos = 2 * kK + 2 * kV;     // the step's column positions (int32)
+    static constexpr int kBytes = kPos + kPfCols * 4;  // k1 | k0 | v1t | v0t | positions
+    static constexpr int kKChunks = kPfCols * D / 8;  // 16-byte pieces of a key tile
+    static constexpr int kVChunks = D * 4;            // 16-byte pieces of a value tile (64 bytes per channel)
+    static constexpr int kPer = (kKChunks + 255) / 256;  // pieces of each tile per thread
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_sparse_kernel(
     const uint16_t* __restrict__ q1, const uint16_t* __restrict__ q0, const int32_t* __restrict__ qpos, int n_q,
     const float* __restrict__ lse0, const float* __restrict__ o0, const uint16_t* __restrict__ k1,
     const uint16_t* __restrict__ k0, const uint16_t* __restrict__ v1t, const uint16_t* __restrict__ v0t, int ldt,
     const int32_t* __restrict__ cpos, int n_c, int H, float sm, float* __restrict__ o32, uint16_t* __restrict__ o16,
     float* __restrict__ mass) {
+    using T = PfTile<D>;
+    static_assert(T::kKChunks == T::kVChunks, "one staging pattern for key and value tiles");
     constexpr int KS = D / 32;   // k-steps of the score products
     constexpr int CB = D / 16;   // 16-channel blocks of the output
+    constexpr int PER = T::kPer;
+    __shared__ __align__(16) uint8_t lds[2][T::kBytes];
     const int h = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, rl = lane & 15;
     const size_t bh = (size_t)b * H + h;
     const int row = blockIdx.x * kPfRows + wave * 16 + rl;
@@ -71,17 +92,56 @@ __global__ __launch_bounds__(256) void prefill_sparse_kernel(
         bq1[ks] = as_bf16x8(ld_u4(q1 + (bh * n_q + rowc) * D + 32 * ks + 8 * g));
         bq0[ks] = as_bf16x8(ld_u4(q0 + (bh * n_q + rowc) * D + 32 * ks + 8 * g));
     }
-    // the columns some row of this wave sees: cpos ascending, so a prefix
-    int last = my_pos;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) last = max(last, __shfl_xor(last, m, 64));
+    // the columns some row of this workgroup sees: cpos ascending, so a prefix
+    const int last = qpos[(size_t)b * n_q + min(n_q, (int)(blockIdx.x + 1) * kPfRows) - 1];
     const int32_t* cp = cpos + bh * n_c;
     int lo = 0, hi = n_c;  // first column with cpos > last
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (cp[mid] <= last) lo = mid + 1; else hi = mid;
     }
-    const int n_vis = lo;
+    const int ntiles = (lo + kPfCols - 1) / kPfCols;
+
+    // staging of a step's tiles: PER 16-byte pieces of each of the four tiles per thread, and
+    // one column position per thread of the first kPfCols (so that the visibility test reads
+    // LDS: waiting on a global load would also wait on the next step's loads issued before it)
+    uint4 st[4][PER];
+    int stpos = 0;
+    auto gload = [&](int c0) {
+        if (tid < kPfCols) stpos = c0 + tid < n_c ? cp[c0 + tid] : 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + 256 * i;
+            if (e < T::kKChunks) {
+                const int col = c0 + e / (D / 8), ch = (e % (D / 8)) * 8;
+                const int colc = col < n_c ? col : n_c - 1;
+                st[0][i] = ld_u4(k1 + (bh * n_c + colc) * D + ch);
+                st[1][i] = ld_u4(k0 + (bh * n_c + colc) * D + ch);
+                const int vc = e >> 2, part = (e & 3) * 8;  // channel, 8 columns of it
+                st[2][i] = ld_u4(v1t + (bh * D + vc) * (size_t)ldt + c0 + part);
+                st[3][i] = ld_u4(v0t + (bh * D + vc) * (size_t)ldt + c0 + part);
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+        uint8_t* base = lds[buf];
+        if (tid < kPfCols) reinterpret_cast<int*>(base + T::kPos)[tid] = stpos;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + 256 * i;
+            if (e < T::kKChunks) {
+                const int kofs = (e / (D / 8)) * T::kKRow + (e % (D / 8)) * 16;
+                *reinterpret_cast<uint4*>(base + kofs) = st[0][i];
+                *reinterpret_cast<uint4*>(base + T::kK + kofs) = st[1][i];
+                const int vofs = (e >> 2) * T::kVRow + (e & 3) * 16;
+                // a 72-byte row keeps 8-byte alignment only: two 8-byte stores
+                *reinterpret_cast<uint2*>(base + 2 * T::kK + vofs) = make_uint2(st[2][i].x, st[2][i].y);
+                *reinterpret_cast<uint2*>(base + 2 * T::kK + vofs + 8) = make_uint2(st[2][i].z, st[2][i].w);
+                *reinterpret_cast<uint2*>(base + 2 * T::kK + T::kV + vofs) = make_uint2(st[3][i].x, st[3][i].y);
+                *reinterpret_cast<uint2*>(base + 2 * T::kK + T::kV + vofs + 8) = make_uint2(st[3][i].z, st[3][i].w);
+            }
+        }
+    };
 
     f32x4_t U[CB], W[CB];
 #pragma unroll
@@ -91,28 +151,33 @@ __global__ __launch_bounds__(256) void prefill_sparse_kernel(
     }
     float M = -__builtin_huge_valf(), Lp = 0.f, mp = 0.f;  // row max; lane-partial sums
 
-    for (int c0 = 0; c0 < n_vis; c0 += kPfCols) {
+    if (ntiles > 0) {
+        gload(0);
+        sstore(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int c0 = t * kPfCols;
+        const uint8_t* base = lds[t & 1];
+        if (t + 1 < ntiles) gload(c0 + kPfCols);   // the next step's tiles, in flight meanwhile
         f32x4_t s1[2], s0[2];
         int cposv[2][4];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             // A operands: key rows of columns c0 + 16 blk + rl
-            const int col = c0 + 16 * blk + rl;
-            const int colc = col < n_c ? col : n_c - 1;
+            const uint8_t* kr = base + (16 * blk + rl) * T::kKRow + 16 * g;
             s1[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             s0[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8_t a1 = as_bf16x8(ld_u4(k1 + (bh * n_c + colc) * D + 32 * ks + 8 * g));
-                const bf16x8_t a0 = as_bf16x8(ld_u4(k0 + (bh * n_c + colc) * D + 32 * ks + 8 * g));
+                const bf16x8_t a1 = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 64 * ks));
+                const bf16x8_t a0 = as_bf16x8(*reinterpret_cast<const uint4*>(kr + T::kK + 64 * ks));
                 s1[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bq1[ks], s1[blk], 0, 0, 0);
                 s0[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq0[ks], s0[blk], 0, 0, 0);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int cj = c0 + 16 * blk + 4 * g + r;   // this lane's column of value r
-                cposv[blk][r] = cj < n_c ? cp[cj] : 0x7FFFFFFF;
-            }
+            for (int r = 0; r < 4; ++r)   // this lane's column of value r (past n_c: never visible)
+                cposv[blk][r] = reinterpret_cast<const int*>(base + T::kPos)[16 * blk + 4 * g + r];
         }
         // probabilities of the preceding loop, and the new logits' running max per row
         float e1[8], p0[8];
@@ -151,16 +216,18 @@ __global__ __launch_bounds__(256) void prefill_sparse_kernel(
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             // A operands: channel 16 cb + rl of the transposed values, the same eight columns
-            const uint16_t* r1 = v1t + (bh * D + 16 * cb + rl) * (size_t)ldt + c0 + 4 * g;
-            const uint16_t* r0 = v0t + (bh * D + 16 * cb + rl) * (size_t)ldt + c0 + 4 * g;
-            const uint2 a1lo = ld_u2(r1), a1hi = ld_u2(r1 + 16);
-            const uint2 a0lo = ld_u2(r0), a0hi = ld_u2(r0 + 16);
+            const uint8_t* vr = base + 2 * T::kK + (16 * cb + rl) * T::kVRow + 8 * g;
+            const uint2 a1lo = *reinterpret_cast<const uint2*>(vr), a1hi = *reinterpret_cast<const uint2*>(vr + 32);
+            const uint2 a0lo = *reinterpret_cast<const uint2*>(vr + T::kV);
+            const uint2 a0hi = *reinterpret_cast<const uint2*>(vr + T::kV + 32);
             U[cb] *= scale;
             U[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(a1lo.x, a1lo.y, a1hi.x, a1hi.y)), pb1,
                                                             U[cb], 0, 0, 0);
             W[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(a0lo.x, a0lo.y, a0hi.x, a0hi.y)), pb0,
                                                             W[cb], 0, 0, 0);
         }
+        if (t + 1 < ntiles) sstore((t + 1) & 1);   // the other buffer: every wave left it a step ago
+        __syncthreads();
     }
     const float L = row_sum4(Lp);
     const float m = row_sum4(mp);

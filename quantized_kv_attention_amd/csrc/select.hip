@@ -11,10 +11,12 @@
 // no other column has that score, a column is taken iff its score is at least the threshold;
 // one scan over per-(row, wave) counts places the selected columns in ascending index order.
 //
-// The fast path is kept small (its unrolled loops carry no mode branches).  Everything
-// else (k >= n, equal, infinite or NaN scores, a crowded threshold bin, a threshold score
-// that other columns share, contexts beyond 40960 columns) goes to plain loops over memory: a 3-pass radix threshold on an
-// order-preserving integer key and a row-by-row compaction.
+// The fast path is kept small (its unrolled loops carry no mode branches); -inf scores
+// (masked columns) stay on it as long as k scores are finite.  Everything else (k >= n,
+// equal scores, +inf or NaN, fewer than k finite scores, a crowded threshold bin, a
+// threshold score that other columns share, contexts beyond 40960 columns) goes to plain
+// loops over memory: a 3-pass radix threshold on an order-preserving integer key and a
+// row-by-row compaction.
 #include "launch.h"
 
 namespace qkv {
@@ -211,11 +213,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
         for (int e = 0; e < kSelPerThread; ++e) v[e] = sc[min(e * kSelThreads + tid, n - 1)];
         for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
         for (int i = tid; i < kCandCap; i += kSelThreads) cand[i] = 0;  // padding ranks below everything
+        // -inf scores (masked columns) take no bin and are never taken here; the k-th score
+        // must be finite, which the histogram below checks (fewer than k finite scores: the
+        // memory paths decide)
         float mn = __builtin_huge_valf(), mx = kNegInf;
         float vsum = 0.f;  // NaN iff some score is NaN (or +inf and -inf meet: not finite either)
 #pragma unroll
         for (int e = 0; e < kSelPerThread; ++e) {
-            mn = fminf(mn, v[e]);
+            mn = fminf(mn, v[e] == kNegInf ? __builtin_huge_valf() : v[e]);
             mx = fmaxf(mx, v[e]);
             vsum += v[e];
         }

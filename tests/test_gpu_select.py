@@ -95,3 +95,19 @@ def test_offset_rows(n):
     for k in (1, -(-n // 10), n - 1):
         say(f"  select offset rows n={n} k={k}")
         run_case(S, lse, k)
+
+
+@pytest.mark.parametrize("n", [4097, 32769])
+def test_masked_scores(n):
+    # most columns masked (-inf), as in a token selection restricted to the preceding set:
+    # k at, below and above the number of finite scores
+    g = np.random.default_rng(n + 5)
+    S = np.full((1, 3, n), -np.inf, np.float32)
+    fin = [n // 4, n // 10, 37]
+    for h, m in enumerate(fin):
+        cols = g.choice(n, m, replace=False)
+        S[0, h, cols] = (g.standard_normal(m) * 0.8).astype(np.float32)
+    lse = np.zeros((1, 3), np.float32)
+    for k in (1, 30, 37, 38, n // 10, n // 10 + 1):
+        say(f"  select masked rows n={n} k={k}")
+        run_case(S, lse, k)
