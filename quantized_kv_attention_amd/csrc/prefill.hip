@@ -29,9 +29,15 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 w) { return __builtin_bit_ca
 __device__ __forceinline__ uint4 ld_u4(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ld_u2(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to bf16 (round to nearest even), a in the low half: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
+
+constexpr float kLog2e = 1.4426950408889634f;
 
 // Max and sum over the four lanes of a wave that hold the same row (lanes l, l ^ 16, l ^ 32, l ^ 48).
 __device__ __forceinline__ float row_max4(float v) {
@@ -42,10 +48,13 @@ __device__ __forceinline__ float row_max4(float v) {
 }
 __device__ __forceinline__ float row_sum4(float v) { return add_xor32(add_xor16(v)); }
 
-constexpr int kPfRows = 64;   // query rows per workgroup (16 per wave)
-constexpr int kPfCols = 32;   // columns per step (two 16-column blocks)
+constexpr int kPfWaves = 8;                 // waves per workgroup
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfRows = 16 * kPfWaves;      // query rows per workgroup (16 per wave): every
+                                            // step's key and value tiles serve all of them
+constexpr int kPfCols = 32;                 // columns per step (two 16-column blocks)
 
-// LDS tiles of one step, shared by the workgroup's four waves: key rows of both loops
+// LDS tiles of one step, shared by the workgroup's waves: key rows of both loops
 // ([column][channel], rows padded by 16 bytes so that the 16 lanes reading 16 columns at one
 // channel offset fall into distinct banks) and transposed values of both loops ([channel]
 // [column], rows of 32 columns padded to 72 bytes for the same reason).
@@ -59,11 +68,11 @@ struct PfTile {
     static constexpr int kBytes = kPos + kPfCols * 4;  // k1 | k0 | v1t | v0t | positions
     static constexpr int kKChunks = kPfCols * D / 8;  // 16-byte pieces of a key tile
     static constexpr int kVChunks = D * 4;            // 16-byte pieces of a value tile (64 bytes per channel)
-    static constexpr int kPer = (kKChunks + 255) / 256;  // pieces of each tile per thread
+    static constexpr int kPer = (kKChunks + kPfThreads - 1) / kPfThreads;  // pieces of each tile per thread
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_sparse_kernel(
+__global__ __launch_bounds__(kPfThreads, 1) void prefill_sparse_kernel(
     const uint16_t* __restrict__ q1, const uint16_t* __restrict__ q0, const int32_t* __restrict__ qpos, int n_q,
     const float* __restrict__ lse0, const float* __restrict__ o0, const uint16_t* __restrict__ k1,
     const uint16_t* __restrict__ k0, const uint16_t* __restrict__ v1t, const uint16_t* __restrict__ v0t, int ldt,
@@ -75,15 +84,20 @@ __global__ __launch_bounds__(256, 2) void prefill_sparse_kernel(
     constexpr int CB = D / 16;   // 16-channel blocks of the output
     constexpr int PER = T::kPer;
     __shared__ __align__(16) uint8_t lds[2][T::kBytes];
-    const int h = blockIdx.y, b = blockIdx.z;
+    // heads vary fastest and row blocks run last to first: the blocks that see the most
+    // columns start first, and the short ones fill the tail
+    const int h = blockIdx.x, b = blockIdx.z;
+    const int rb = gridDim.y - 1 - blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, rl = lane & 15;
     const size_t bh = (size_t)b * H + h;
-    const int row = blockIdx.x * kPfRows + wave * 16 + rl;
+    const int row = rb * kPfRows + wave * 16 + rl;
     const bool rvalid = row < n_q;
     const int rowc = rvalid ? row : n_q - 1;
     const int my_pos = rvalid ? qpos[(size_t)b * n_q + row] : -1;
-    const float my_lse = lse0[bh * n_q + rowc];
+    // exponentials as 2^x: the scale and the row's lse carry the factor log2(e)
+    const float sm2 = sm * kLog2e;
+    const float my_lse2 = lse0[bh * n_q + rowc] * kLog2e;
 
     // B operands of S^T = K Q^T: this lane's row, channels 32 ks + 8 g .. + 7
     bf16x8_t bq1[KS], bq0[KS];
@@ -93,7 +107,7 @@ __global__ __launch_bounds__(256, 2) void prefill_sparse_kernel(
         bq0[ks] = as_bf16x8(ld_u4(q0 + (bh * n_q + rowc) * D + 32 * ks + 8 * g));
     }
     // the columns some row of this workgroup sees: cpos ascending, so a prefix
-    const int last = qpos[(size_t)b * n_q + min(n_q, (int)(blockIdx.x + 1) * kPfRows) - 1];
+    const int last = qpos[(size_t)b * n_q + min(n_q, (rb + 1) * kPfRows) - 1];
     const int32_t* cp = cpos + bh * n_c;
     int lo = 0, hi = n_c;  // first column with cpos > last
     while (lo < hi) {
@@ -111,7 +125,7 @@ __global__ __launch_bounds__(256, 2) void prefill_sparse_kernel(
         if (tid < kPfCols) stpos = c0 + tid < n_c ? cp[c0 + tid] : 0x7FFFFFFF;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int e = tid + 256 * i;
+            const int e = tid + kPfThreads * i;
             if (e < T::kKChunks) {
                 const int col = c0 + e / (D / 8), ch = (e % (D / 8)) * 8;
                 const int colc = col < n_c ? col : n_c - 1;
@@ -128,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void prefill_sparse_kernel(
         if (tid < kPfCols) reinterpret_cast<int*>(base + T::kPos)[tid] = stpos;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int e = tid + 256 * i;
+            const int e = tid + kPfThreads * i;
             if (e < T::kKChunks) {
                 const int kofs = (e / (D / 8)) * T::kKRow + (e % (D / 8)) * 16;
                 *reinterpret_cast<uint4*>(base + kofs) = st[0][i];
@@ -156,6 +170,10 @@ __global__ __launch_bounds__(256, 2) void prefill_sparse_kernel(
         sstore(0);
     }
     __syncthreads();
+    // every load issued so far (the query operands above all) has landed: without this wait
+    // the compiler's counter tracking, merging the paths into the loop, would make the first
+    // use of those operands in each step wait for the next step's tiles as well
+    __builtin_amdgcn_s_waitcnt(0);
     for (int t = 0; t < ntiles; ++t) {
         const int c0 = t * kPfCols;
         const uint8_t* base = lds[t & 1];
@@ -179,7 +197,8 @@ __global__ __launch_bounds__(256, 2) void prefill_sparse_kernel(
             for (int r = 0; r < 4; ++r)   // this lane's column of value r (past n_c: never visible)
                 cposv[blk][r] = reinterpret_cast<const int*>(base + T::kPos)[16 * blk + 4 * g + r];
         }
-        // probabilities of the preceding loop, and the new logits' running max per row
+        // probabilities of the preceding loop, and the new logits' running max per row (the
+        // logits in log2 units)
         float e1[8], p0[8];
         float tmax = -__builtin_huge_valf();
 #pragma unroll
@@ -187,22 +206,21 @@ __global__ __launch_bounds__(256, 2) void prefill_sparse_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const bool vis = cposv[blk][r] <= my_pos;
-                const float s = sm * s1[blk][r];
-                e1[4 * blk + r] = vis ? s : -__builtin_huge_valf();
-                p0[4 * blk + r] = vis ? __expf(fmaf(sm, s0[blk][r], -my_lse)) : 0.f;
+                e1[4 * blk + r] = vis ? sm2 * s1[blk][r] : -__builtin_huge_valf();
+                p0[4 * blk + r] = vis ? __builtin_amdgcn_exp2f(fmaf(sm2, s0[blk][r], -my_lse2)) : 0.f;
                 tmax = fmaxf(tmax, e1[4 * blk + r]);
             }
         }
         tmax = row_max4(tmax);
         const float Mn = fmaxf(M, tmax);
-        const float scale = (M == -__builtin_huge_valf()) ? 0.f : __expf(M - Mn);
+        const float scale = (M == -__builtin_huge_valf()) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
         M = Mn;
         uint32_t w1[4], w0[4];
         float lsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-            const float x0 = e1[e] == -__builtin_huge_valf() ? 0.f : __expf(e1[e] - Mn);
-            const float x1 = e1[e + 1] == -__builtin_huge_valf() ? 0.f : __expf(e1[e + 1] - Mn);
+            const float x0 = e1[e] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(e1[e] - Mn);
+            const float x1 = e1[e + 1] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(e1[e + 1] - Mn);
             w1[e / 2] = pack_bf16(x0, x1);
             w0[e / 2] = pack_bf16(p0[e], p0[e + 1]);
             // the normalisation sums the weights the product uses (bf16)
@@ -213,6 +231,11 @@ __global__ __launch_bounds__(256, 2) void prefill_sparse_kernel(
         // B operands of O^T = V^T P^T: element e is column 4 g + e (e < 4) or 16 + 4 g + (e - 4)
         const bf16x8_t pb1 = as_bf16x8(make_uint4(w1[0], w1[1], w1[2], w1[3]));
         const bf16x8_t pb0 = as_bf16x8(make_uint4(w0[0], w0[1], w0[2], w0[3]));
+        // the running sums need rescaling only where some row's max moved
+        if (__ballot(scale != 1.f)) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) U[cb] *= scale;
+        }
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             // A operands: channel 16 cb + rl of the transposed values, the same eight columns
@@ -220,7 +243,6 @@ __global__ __launch_bounds__(256, 2) void prefill_sparse_kernel(
             const uint2 a1lo = *reinterpret_cast<const uint2*>(vr), a1hi = *reinterpret_cast<const uint2*>(vr + 32);
             const uint2 a0lo = *reinterpret_cast<const uint2*>(vr + T::kV);
             const uint2 a0hi = *reinterpret_cast<const uint2*>(vr + T::kV + 32);
-            U[cb] *= scale;
             U[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(a1lo.x, a1lo.y, a1hi.x, a1hi.y)), pb1,
                                                             U[cb], 0, 0, 0);
             W[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(a0lo.x, a0lo.y, a0hi.x, a0hi.y)), pb0,
@@ -298,12 +320,12 @@ int launch_prefill_sparse(int B, int H, int D, const uint16_t* q1, const uint16_
                           const uint16_t* v1t, const uint16_t* v0t, const int32_t* cpos, int n_c, float sm,
                           float* o32, uint16_t* o16, float* mass, hipStream_t st) {
     const int ldt = ((n_c + 31) / 32) * 32;
-    dim3 grid((n_q + kPfRows - 1) / kPfRows, H, B);
+    dim3 grid(H, (n_q + kPfRows - 1) / kPfRows, B);
     if (D == 128)
-        prefill_sparse_kernel<128><<<grid, 256, 0, st>>>(q1, q0, qpos, n_q, lse0, o0, k1, k0, v1t, v0t, ldt, cpos,
+        prefill_sparse_kernel<128><<<grid, kPfThreads, 0, st>>>(q1, q0, qpos, n_q, lse0, o0, k1, k0, v1t, v0t, ldt, cpos,
                                                          n_c, H, sm, o32, o16, mass);
     else
-        prefill_sparse_kernel<64><<<grid, 256, 0, st>>>(q1, q0, qpos, n_q, lse0, o0, k1, k0, v1t, v0t, ldt, cpos,
+        prefill_sparse_kernel<64><<<grid, kPfThreads, 0, st>>>(q1, q0, qpos, n_q, lse0, o0, k1, k0, v1t, v0t, ldt, cpos,
                                                         n_c, H, sm, o32, o16, mass);
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
 }
