@@ -136,6 +136,15 @@ def test_all_columns_is_dense_on_gpu():
         assert rel < 1e-5
 
 
+@pytest.mark.parametrize("d,n,k", [(128, 4000, 60), (64, 3000, 110)])
+def test_selection_spread_over_many_key_groups(d, n, k):
+    # a few columns over a long context: a chunk's columns fall in more distinct key groups
+    # than a workgroup stages, so the columns past them read their own group metadata
+    w = dataclasses.replace(W["ctx4k"] if d == 128 else W["tiny"], H=2)
+    p = Pair(w, n=n, extra=8)
+    check_step(p, p.queries(5), w.n_dense, k, f"n={n} k={k} d={d}")
+
+
 def test_no_columns_keeps_previous_output():
     w = W["tiny"]
     p = Pair(w, extra=8)
