@@ -63,7 +63,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-entry-point measurements")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and components")
-    ap.add_argument("--only", choices=["headline", "c1", "c3", "c4", "codecs", "tokens", "prefill"],
+    ap.add_argument("--only", choices=["headline", "c1", "c3", "c4", "codecs", "tokens", "prefill", "shard"],
                     help="run one section only (for kernel traces)")
     ap.add_argument("--profile", choices=sorted(TRAFFIC), help="only launch one kernel family (counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -562,6 +562,29 @@ def graph_step_row(rot, reps=10):
     return us, nbytes, loop_bytes
 
 
+def extra_shard(args):
+    """One GPU's share of the 32K step when the 16 heads are sharded over 8 GPUs: 2 heads x 128
+    at 32K, 8 rotated layers, graph replay, flush not included.  The kernels are the same; the
+    dense plan sizes its splits for the smaller head count."""
+    import dataclasses
+
+    from quantized_kv_attention_amd import synth
+    w = dataclasses.replace(synth.WORKLOADS["ctx32k"], H=2)
+    rot = Rotation(w, 8, seed=600)
+    us, nbytes, lb = graph_step_row(rot)
+    say(f"shard (2 heads x 32K): {us:.1f} us per layer-step ({nbytes / 1e6:.1f} MB, {nbytes / us / 1e3:.0f} GB/s)")
+    loop_bytes, flush_loop, append_bytes, full_chain = rot.step_bytes()
+    rows = measure_rows(rot, loop_bytes, flush_loop, append_bytes, full_chain)
+    keep = {k_: v for k_, v in rows.items() if k_.startswith("attn_decode_") and "flush" not in k_}
+    for k_, v in keep.items():
+        say(f"  shard {k_}: {v['us']:.2f} us ({v['GBps']:.0f} GB/s)")
+    out = row(us, nbytes, bytes_per_loop=[int(x) for x in lb], calls=keep,
+              workload="2 heads x 128 at 32K (one GPU's share of 16 heads over 8 GPUs), 8 rotated layers, "
+                       "graph replay, flush not included")
+    del rot
+    return out
+
+
 def extra_c3(args):
     """40 heads x 128, 8K context, 32 loops (2 dense + 30 sparse loops over the full chain)."""
     from quantized_kv_attention_amd import synth
@@ -944,7 +967,7 @@ def main():
         return
     w = synth.WORKLOADS["ctx32k"]
     sections = {"c1": extra_c1, "c3": extra_c3, "c4": extra_c4, "codecs": extra_codecs, "tokens": extra_tokens,
-                "prefill": extra_prefill}
+                "prefill": extra_prefill, "shard": extra_shard}
     if args.only and args.only != "headline":
         res = sections[args.only](args)
         print(json.dumps({"section": args.only, "result": res}), flush=True)

@@ -25,10 +25,16 @@
 
 namespace qkv {
 
-constexpr int kWaveRounds = 3;                 // column rounds per wave
+// Column rounds per wave: three when the launch has waves enough for two or more per SIMD at
+// three rounds (a 32K context over 16 heads: 4 416 waves, all resident at 5 per SIMD), two for
+// smaller launches, whose waves then carry shorter chains of dependent loads (2 heads x 32K,
+// one GPU's share of 16 heads over 8: 65.0 against 72.3 us per layer-step, one round 65.7).
+constexpr int kWaveRounds = 3;
+constexpr int kWaveRoundsSmall = 2;
+constexpr int kSmallLaunchWaves = 2048;        // fewer waves than this at three rounds: two rounds
 // selected columns per workgroup (4 waves): d/8 lanes per column, 64 / (d/8) per round
 constexpr int kSpWaves = 4;                    // waves per workgroup
-constexpr int chunk_cols(int D) { return kSpWaves * kWaveRounds * (64 / (D / 8)); }
+constexpr int chunk_cols(int D, int rounds = kWaveRounds) { return kSpWaves * rounds * (64 / (D / 8)); }
 // A chunk's partial record: [max, sum, -, -, U[0..D), W[0..D)], 16-byte aligned.
 constexpr int sp_record(int D) { return 2 * D + 4; }
 
@@ -81,7 +87,7 @@ __device__ __forceinline__ void store_new_row(NewRow nr, uint16_t* tk, uint16_t*
 // (the host passes the planes from the last dense one before `loop` on).
 // FLUSH: extra workgroups past the chunks encode this loop's 64-row tail flush (FlushArg);
 // the chunks never read those rows' plane slots in this launch.
-template <int D, int SB, int RB, bool REPLACE, bool FLUSH>
+template <int D, int SB, int RB, bool REPLACE, bool FLUSH, int ROUNDS = kWaveRounds>
 __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 1) void sparse_chunk_kernel(CacheArg ca, int loop, const uint16_t* __restrict__ q,
                                                            NewRow nr, float sm, const int32_t* __restrict__ idx,
                                                            const float* __restrict__ p_sel, int k,
@@ -96,9 +102,8 @@ __global__ __launch_bounds__(64 * kSpWaves, SB > 1 ? 3 : 1) void sparse_chunk_ke
     }
     constexpr int LPC = D / 8;             // lanes per column
     constexpr int CPR = 64 / LPC;          // columns per wave round
-    constexpr int ROUNDS = kWaveRounds;
     constexpr int kWaveCols = ROUNDS * CPR;
-    constexpr int kChunk = chunk_cols(D);
+    constexpr int kChunk = chunk_cols(D, ROUNDS);
     static_assert(kChunk == kSpWaves * kWaveCols, "a chunk is the workgroup's columns");
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -532,14 +537,27 @@ __global__ __launch_bounds__(D) void sparse_copy_kernel(const float* o_prev, uin
 
 // workspace: chunk partials [B][H][nchunk][2 + 2D], then the raw selected scores [B][H][k]
 size_t sparse_ws_bytes(int B, int H, int D, int k) {
-    const int nchunk = (k + chunk_cols(D) - 1) / chunk_cols(D);
+    const int cc = chunk_cols(D, kWaveRoundsSmall);   // the smaller chunks: the most records
+    const int nchunk = (k + cc - 1) / cc;
     return (size_t)B * H * nchunk * sp_record(D) * sizeof(float) + (size_t)B * H * k * sizeof(float);
 }
 
 int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow nr, float sm, const int32_t* idx,
                   const float* p_sel, const float* mass, int k, const float* o_prev, const float* lse,
                   float* scores, int ld, uint16_t* o, float* o32, void* ws, hipStream_t st, FlushArg fl) {
-    const int nchunk = (k + chunk_cols(D) - 1) / chunk_cols(D);
+    // full-state codec: the planes from the last dense one before `loop` on
+    int lv = loop;
+    const CacheArg v = ca.full ? full_state_view(ca, loop - 1, &lv) : ca;
+    if (ca.full) lv += 1;  // the view was taken for loop - 1
+    // deep chains: batched loads (and long chains first), which need every plane of the
+    // chain to hold a block
+    bool batched = lv > 4;
+    for (int p = 0; batched && p < lv; ++p) batched = v.p[p].data != nullptr && v.p[p].n_blocks > 0;
+    // rounds per wave: two for launches too small to fill the chip at three
+    const long waves3 = (long)((k + chunk_cols(D) - 1) / chunk_cols(D)) * ca.H * ca.B * kSpWaves;
+    const bool small = !batched && waves3 < kSmallLaunchWaves;
+    const int ccols = small ? chunk_cols(D, kWaveRoundsSmall) : chunk_cols(D);
+    const int nchunk = (k + ccols - 1) / ccols;
     uint16_t* tk = const_cast<uint16_t*>(ca.tail_k[loop - 1]);
     uint16_t* tv = const_cast<uint16_t*>(ca.tail_v[loop - 1]);
     const int slot = (ca.n_ctx - 1) % kTail;
@@ -557,14 +575,6 @@ int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow
     float* part = static_cast<float*>(ws);
     float* cs = scores ? part + (size_t)ca.B * ca.H * nchunk * sp_record(D) : nullptr;  // raw scores for the splice
     dim3 grid(nchunk, ca.H, ca.B);
-    // full-state codec: the planes from the last dense one before `loop` on
-    int lv = loop;
-    const CacheArg v = ca.full ? full_state_view(ca, loop - 1, &lv) : ca;
-    if (ca.full) lv += 1;  // the view was taken for loop - 1
-    // deep chains: batched loads (and long chains first), which need every plane of the
-    // chain to hold a block
-    bool batched = lv > 4;
-    for (int p = 0; batched && p < lv; ++p) batched = v.p[p].data != nullptr && v.p[p].n_blocks > 0;
     if (fl.pos0 >= 0) fl.loop = lv;
     const int extra = flush_groups(fl, !ca.p[loop - 1].dense);
     grid.x += extra;
@@ -573,12 +583,17 @@ int launch_sparse(const CacheArg& ca, int D, int loop, const uint16_t* q, NewRow
         constexpr int DD = decltype(dc)::value, RBB = decltype(rbc)::value;
         constexpr bool FF = decltype(fullc)::value;
         if (!batched) {
-            if (extra)
-                sparse_chunk_kernel<DD, 1, RBB, FF, true><<<grid, 64 * kSpWaves, dyn, st>>>(v, lv, q, nr, sm, idx, p_sel,
-                                                                                        k, cs, part, nchunk, fl);
-            else
-                sparse_chunk_kernel<DD, 1, RBB, FF, false><<<grid, 64 * kSpWaves, 0, st>>>(v, lv, q, nr, sm, idx, p_sel,
-                                                                                       k, cs, part, nchunk, fl);
+            auto go = [&](auto rc) {
+                constexpr int RR = decltype(rc)::value;
+                if (extra)
+                    sparse_chunk_kernel<DD, 1, RBB, FF, true, RR><<<grid, 64 * kSpWaves, dyn, st>>>(
+                        v, lv, q, nr, sm, idx, p_sel, k, cs, part, nchunk, fl);
+                else
+                    sparse_chunk_kernel<DD, 1, RBB, FF, false, RR><<<grid, 64 * kSpWaves, 0, st>>>(
+                        v, lv, q, nr, sm, idx, p_sel, k, cs, part, nchunk, fl);
+            };
+            if (small) go(std::integral_constant<int, kWaveRoundsSmall>{});
+            else go(std::integral_constant<int, kWaveRounds>{});
         } else {
             if (extra)
                 sparse_chunk_kernel<DD, 3, RBB, FF, true><<<grid, 64 * kSpWaves, dyn, st>>>(v, lv, q, nr, sm, idx, p_sel,
