@@ -108,6 +108,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_sparse_kernel(
     }
     // the columns some row of this workgroup sees: cpos ascending, so a prefix
     const int last = qpos[(size_t)b * n_q + min(n_q, (rb + 1) * kPfRows) - 1];
+    const int first_pos = qpos[(size_t)b * n_q + rb * kPfRows];   // the workgroup's first row
     const int32_t* cp = cpos + bh * n_c;
     int lo = 0, hi = n_c;  // first column with cpos > last
     while (lo < hi) {
@@ -198,30 +199,51 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_sparse_kernel(
                 cposv[blk][r] = reinterpret_cast<const int*>(base + T::kPos)[16 * blk + 4 * g + r];
         }
         // probabilities of the preceding loop, and the new logits' running max per row (the
-        // logits in log2 units)
+        // logits in log2 units).  A step whose last column precedes the workgroup's first row
+        // is visible to every row: no masks (all but a workgroup's last few steps).
+        const bool full = reinterpret_cast<const int*>(base + T::kPos)[kPfCols - 1] <= first_pos;
         float e1[8], p0[8];
         float tmax = -__builtin_huge_valf();
+        if (full) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
+            for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool vis = cposv[blk][r] <= my_pos;
-                e1[4 * blk + r] = vis ? sm2 * s1[blk][r] : -__builtin_huge_valf();
-                p0[4 * blk + r] = vis ? __builtin_amdgcn_exp2f(fmaf(sm2, s0[blk][r], -my_lse2)) : 0.f;
-                tmax = fmaxf(tmax, e1[4 * blk + r]);
+                for (int r = 0; r < 4; ++r) {
+                    e1[4 * blk + r] = sm2 * s1[blk][r];
+                    p0[4 * blk + r] = __builtin_amdgcn_exp2f(fmaf(sm2, s0[blk][r], -my_lse2));
+                    tmax = fmaxf(tmax, e1[4 * blk + r]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool vis = cposv[blk][r] <= my_pos;
+                    e1[4 * blk + r] = vis ? sm2 * s1[blk][r] : -__builtin_huge_valf();
+                    p0[4 * blk + r] = vis ? __builtin_amdgcn_exp2f(fmaf(sm2, s0[blk][r], -my_lse2)) : 0.f;
+                    tmax = fmaxf(tmax, e1[4 * blk + r]);
+                }
             }
         }
         tmax = row_max4(tmax);
         const float Mn = fmaxf(M, tmax);
         const float scale = (M == -__builtin_huge_valf()) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
         M = Mn;
+        float x[8];
+        if (full) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = __builtin_amdgcn_exp2f(e1[e] - Mn);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                x[e] = e1[e] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(e1[e] - Mn);
+        }
         uint32_t w1[4], w0[4];
         float lsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-            const float x0 = e1[e] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(e1[e] - Mn);
-            const float x1 = e1[e + 1] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(e1[e + 1] - Mn);
-            w1[e / 2] = pack_bf16(x0, x1);
+            w1[e / 2] = pack_bf16(x[e], x[e + 1]);
             w0[e / 2] = pack_bf16(p0[e], p0[e + 1]);
             // the normalisation sums the weights the product uses (bf16)
             lsum += bf16_to_f32(w1[e / 2] & 0xFFFFu) + bf16_to_f32(w1[e / 2] >> 16);
