@@ -63,39 +63,42 @@ __global__ __launch_bounds__(64 * kTokWaves) void token_score_kernel(const uint1
 
 // Drops the selected entries whose score is -inf (tokens outside the preceding set, picked
 // only when k exceeds its size), in place and in order; writes the count and the count of
-// positions below `split`.  One workgroup per sequence.
-__global__ __launch_bounds__(256) void token_compact_kernel(const float* __restrict__ score, int n, int k,
-                                                            int32_t* __restrict__ act_out, int32_t* __restrict__ n_out,
-                                                            int32_t* __restrict__ n_before, int split) {
+// positions below `split`.  One workgroup of kCompactWaves waves per sequence.
+constexpr int kCompactWaves = 16;
+constexpr int kCompactThreads = 64 * kCompactWaves;
+
+__global__ __launch_bounds__(kCompactThreads) void token_compact_kernel(const float* __restrict__ score, int n, int k,
+                                                                        int32_t* __restrict__ act_out,
+                                                                        int32_t* __restrict__ n_out,
+                                                                        int32_t* __restrict__ n_before, int split) {
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int32_t* a = act_out + (size_t)b * k;
-    __shared__ uint32_t wcnt[4], wlow[4];
+    __shared__ uint32_t wcnt[kCompactWaves], wlow[kCompactWaves];
     uint32_t base = 0, below = 0;
-    for (int i0 = 0; i0 < k; i0 += 256) {
+    for (int i0 = 0; i0 < k; i0 += kCompactThreads) {
         const int i = i0 + tid;
         const int t = i < k ? a[i] : -1;
         const bool keep = t >= 0 && t < n && score[(size_t)b * n + t] > -__builtin_huge_valf();
         const uint64_t bal = __ballot(keep);
-        if (lane == 0) wcnt[wave] = (uint32_t)__popcll(bal);
+        // positions below the split: the kept entries are ascending
+        const uint64_t bs = __ballot(keep && t < split);
+        if (lane == 0) {
+            wcnt[wave] = (uint32_t)__popcll(bal);
+            wlow[wave] = (uint32_t)__popcll(bs);
+        }
         __syncthreads();  // every entry of this chunk has been read
-        uint32_t before = 0, all = 0;
+        uint32_t before = 0, all = 0, low = 0;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < kCompactWaves; ++w) {
             before += w < wave ? wcnt[w] : 0u;
             all += wcnt[w];
+            low += wlow[w];
         }
         const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
         if (keep) a[base + before + (uint32_t)__popcll(bal & lower)] = t;  // never past entry i
-        // positions below the split: the kept entries are ascending
-        const uint64_t bs = __ballot(keep && t < split);
-        if (lane == 0) wlow[wave] = (uint32_t)__popcll(bs);
-        __syncthreads();
-        uint32_t bsum = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) bsum += wlow[w];
-        below += bsum;
+        below += low;
         base += all;
-        __syncthreads();
+        __syncthreads();  // the counts are read before the next chunk writes them
     }
     if (tid == 0) {
         n_out[b] = (int32_t)base;
@@ -118,7 +121,7 @@ int launch_select_tokens(const uint16_t* hc, const uint16_t* hp, int ld_tok, int
     if (hipGetLastError() != hipSuccess) return QKV_ELAUNCH;
     const int rc = launch_select(score, n, zlse, B, 1, n, k, act_out, p_sel, mass, nullptr, st);
     if (rc != QKV_OK) return rc;
-    token_compact_kernel<<<B, 256, 0, st>>>(score, n, k, act_out, n_out, n_before, split);
+    token_compact_kernel<<<B, kCompactThreads, 0, st>>>(score, n, k, act_out, n_out, n_before, split);
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
 }
 
