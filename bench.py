@@ -387,10 +387,10 @@ def measure_rows(rot, loop_bytes, flush_loop, append_bytes, full_chain):
     t = timed(lambda: [qkv.attn_decode_dense(ly["c"], R, ly["q"][R - 1], 1.0, ly["b"].o[R - 1], ly["b"].o_f32[R - 1],
                                              ly["b"].scores, ly["b"].lse, ly["b"].ws, s) for ly in layers], 3) / L
     out[f"attn_decode_dense loop {R} (full chain, for comparison)"] = row(t, full_chain)
-    t = timed(lambda: [qkv.kv_append_tail(ly["c"], 0, rot.n_step - 1, torch.stack([x.view(w.B, w.H, 1, w.d)
-                                                                                   for x in ly["kn"]]),
-                                          torch.stack([x.view(w.B, w.H, 1, w.d) for x in ly["vn"]]), s)
-                       for ly in layers], 3) / L
+    rows_kv = [(torch.stack([x.view(w.B, w.H, 1, w.d) for x in ly["kn"]]),
+                torch.stack([x.view(w.B, w.H, 1, w.d) for x in ly["vn"]])) for ly in layers]   # built untimed
+    t = timed(lambda: [qkv.kv_append_tail(ly["c"], 0, rot.n_step - 1, kv[0], kv[1], s)
+                       for ly, kv in zip(layers, rows_kv)], 3) / L
     out["kv_append_tail (all loops; the step stores rows inside the attention calls)"] = row(t, append_bytes, "latency")
     for r in range(w.R):
         def fl(ly, r=r):
