@@ -479,7 +479,8 @@ def read_ceiling():
 
 
 def profile_run(args, rot):
-    """Launches only one kernel family (warmup + steps calls over the layers), for counters."""
+    """For counter runs: one warm-up step of every loop (the sparse calls need its scores and
+    selections), then warmup + steps calls of one kernel family over the layers."""
     import torch
     import quantized_kv_attention_amd as qkv
     w, s = rot.w, torch.cuda.current_stream()
@@ -898,16 +899,34 @@ def summarize_trace(args):
     print("\n".join(lines))
 
 
-def _counter_per_dispatch(d, counter, names):
+def _counter_per_dispatch(d, counter, names, last=None):
+    """Mean counter value per dispatch of each kernel name (substring), over its `last`
+    dispatches in dispatch order when given (the profiled calls come after a warm-up step
+    whose dispatches of the same kernel, e.g. another loop's, must not enter the mean)."""
     con = _rocprof_db(d)
     vals = {}
-    for name, cn, cv in con.execute("select name, counter_name, counter_value from pmc_events"):
+    for name, did, cn, cv in con.execute("select name, dispatch_id, counter_name, counter_value from pmc_events"):
         if cn != counter:
             continue
         for k in names:
             if k in name:
-                vals.setdefault(k, []).append(float(cv))
-    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+                vals.setdefault(k, []).append((int(did), float(cv)))
+    out = {}
+    for k, v in vals.items():
+        v.sort()
+        if last:
+            v = v[-last:]
+        out[k] = (sum(x for _, x in v) / len(v), len(v))
+    return out
+
+
+# Dispatches of each kernel of a family that `--profile <key> --steps 2 --warmup 1` makes
+# after its warm-up step: (1 + 2) calls over the 8 rotated layers, or 1 + 2 selections.
+PROFILE_STEPS, PROFILE_WARMUP = 2, 1
+
+
+def profiled_dispatches(key, layers=8):
+    return (PROFILE_STEPS + PROFILE_WARMUP) * (1 if key == "select" else layers)
 
 
 def summarize_traffic(args):
@@ -922,8 +941,9 @@ def summarize_traffic(args):
         raise SystemExit("copy calibration dispatches not found")
     f_fac = COPY_BYTES / (cf[0] * 1024.0)
     w_fac = COPY_BYTES / (cw[0] * 1024.0)
-    fe = _counter_per_dispatch(fdir, "FETCH_SIZE", kernels)
-    wr = _counter_per_dispatch(wdir, "WRITE_SIZE", kernels)
+    n_last = profiled_dispatches(key)
+    fe = _counter_per_dispatch(fdir, "FETCH_SIZE", kernels, n_last)
+    wr = _counter_per_dispatch(wdir, "WRITE_SIZE", kernels, n_last)
     rd = sum(fe[k][0] for k in fe) * 1024.0 * f_fac
     wt = sum(wr[k][0] for k in wr) * 1024.0 * w_fac
     lines = [f"# HBM traffic of {key} at 32K context (16 heads x 128; one launch = {' + '.join(kernels)})",
