@@ -111,3 +111,23 @@ def test_masked_scores(n):
     for k in (1, 30, 37, 38, n // 10, n // 10 + 1):
         say(f"  select masked rows n={n} k={k}")
         run_case(S, lse, k)
+
+
+@pytest.mark.parametrize("n", [4097, 32769, 40960])
+def test_skewed_rows(n):
+    # heavy-tailed scores (log-normal, as the token-change ratios are): most columns share the
+    # lowest bins of [min, max], so the threshold bin can be crowded past the exact-ranking
+    # capacity (then the radix path decides); with exact duplicates planted around the k-th
+    # score, and -inf columns
+    g = np.random.default_rng(n + 17)
+    S = np.zeros((1, 4, n), np.float32)
+    for h, sig in enumerate((1.5, 3.0, 6.0, 1.5)):
+        S[0, h] = np.exp(sig * g.standard_normal(n)).astype(np.float32)
+    S[0, 3, ::5] = -np.inf
+    srt = np.sort(S[0, 1])[::-1]
+    S[0, 1, g.choice(n, 5, replace=False)] = srt[n // 4 - 1]   # a shared score near k = n/4
+    mx = S.max(-1, keepdims=True)
+    lse = (np.log(np.exp((S - mx).astype(np.float64)).sum(-1)) + mx[..., 0]).astype(np.float32)
+    for k in (1, -(-n // 10), n // 4, n // 4 + 2, n // 2, n - 1):
+        say(f"  select skewed rows n={n} k={k}")
+        run_case(S, lse, k)
