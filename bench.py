@@ -434,9 +434,9 @@ def rooflines(rows, loop_bytes, w, rot):
     entry("dense2", "dense_split_kernel<128,2> + dense_combine_kernel<128> (loop 2: base + residual plane)",
           d2["us"], d2["bytes"], d2["us"])
     s3, s4 = rows["attn_decode_sparse loop 3"], rows["attn_decode_sparse loop 4"]
-    entry("sparse3", "sparse_chunk_kernel<128,1> + sparse_combine_kernel<128> (loop 3)", s3["us"], s3["bytes"],
+    entry("sparse3", "sparse_chunk_kernel<128> + sparse_combine_kernel<128> (loop 3)", s3["us"], s3["bytes"],
           s3["us"])
-    entry("sparse4", "sparse_chunk_kernel<128,1> + sparse_combine_kernel<128> (loop 4)", s4["us"], s4["bytes"],
+    entry("sparse4", "sparse_chunk_kernel<128> + sparse_combine_kernel<128> (loop 4)", s4["us"], s4["bytes"],
           s4["us"])
     sel = [v for k_, v in rows.items() if k_.startswith("select_columns") and "layers per call" in k_]
     if sel:   # one launch selects for every rotated layer
@@ -446,7 +446,7 @@ def rooflines(rows, loop_bytes, w, rot):
     # the step's largest share: the sparse gather runs twice (loops 3 and 4)
     fams = {"dense_split_kernel<128,2> (loop 2)": (d2["us"], d2["bytes"], "dense2", d2["us"]),
             "dense_split_kernel<128,1> (loop 1)": (d1["us"], d1["bytes"], "dense1", d1["us"]),
-            "sparse_chunk_kernel<128,1> (loops 3 and 4)": ((s3["us"] + s4["us"]) / 2, (s3["bytes"] + s4["bytes"]) / 2,
+            "sparse_chunk_kernel<128> (loops 3 and 4)": ((s3["us"] + s4["us"]) / 2, (s3["bytes"] + s4["bytes"]) / 2,
                                                           None, s3["us"] + s4["us"])}
     name, (us, nbytes, key, share) = max(fams.items(), key=lambda kv: kv[1][3])
     if key is None:
