@@ -4,26 +4,28 @@
 //
 // Order: fp32 score descending, ties to the lower index; +0 and -0 compare equal.
 // One 1024-thread workgroup per (sequence, head).  Thread t keeps columns t, t+1024, ...
-// (up to 40 of them) in registers.  A histogram over 2048 equal-width value bins between
-// the smallest and largest score finds the bin holding the k-th column (bins are a monotone
-// function of the score, so every bin above it is taken whole); the few columns of that
-// bin are ranked exactly as 64-bit (key, index) words, which gives the threshold score.  When
-// no other column has that score, a column is taken iff its score is at least the threshold;
-// one scan over per-(row, wave) counts places the selected columns in ascending index order.
+// (up to PT of them: 10, 20 or 40, the fewest that hold the row) in registers.  A histogram
+// over 2048 equal-width value bins between the smallest and largest score finds the bin
+// holding the k-th column (bins are a monotone function of the score, so every bin above it
+// is taken whole); the few columns of that bin are ranked exactly as 64-bit (key, index)
+// words, which gives the threshold word (x_t, j_t).  A column is taken iff its score is above
+// x_t, or equal to it at an index up to j_t: ties across the threshold are decided here too.
+// One scan over per-(row, wave) counts places the selected columns in ascending index order.
 //
 // The fast path is kept small (its unrolled loops carry no mode branches); -inf scores
 // (masked columns) stay on it as long as k scores are finite.  Everything else (k >= n,
-// equal scores, +inf or NaN, fewer than k finite scores, a crowded threshold bin, a
-// threshold score that other columns share, contexts beyond 40960 columns) goes to plain
-// loops over memory: a 3-pass radix threshold on an order-preserving integer key and a
-// row-by-row compaction.
+// all scores equal, +inf or NaN, fewer than k finite scores, a crowded threshold bin,
+// contexts beyond 40960 columns) goes to plain loops over memory: a 3-pass radix threshold
+// on an order-preserving integer key and a row-by-row compaction.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace qkv {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelPerThread = 40;      // register-resident scores per thread (n <= 40960)
+constexpr int kSelPerThread = 40;      // register-resident scores per thread at most (n <= 40960)
 constexpr int kBins = 2048;
 constexpr int kCandCap = 2048;         // threshold-bin columns ranked exactly
 constexpr int kStage = 4096;           // selections staged in LDS for coalesced stores
@@ -173,6 +175,7 @@ __device__ __noinline__ float compact_memory(const float* sc, int n, bool take_a
     return psum;
 }
 
+template <int PT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ scores, int ld,
                                                              const float* __restrict__ lse, int n, int k,
                                                              int32_t* __restrict__ idx, float* __restrict__ p_sel,
@@ -188,8 +191,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
     __shared__ uint32_t bcast[4];
     __shared__ uint64_t cand[kCandCap];
     __shared__ uint64_t thr_sh;
-    __shared__ uint32_t thr_unique;
-    __shared__ uint32_t row_off[kSelPerThread * kSelWaves];  // [row][wave]: counts, then offsets
+    __shared__ uint32_t thr_found;
+    __shared__ uint32_t row_off[PT * kSelWaves];  // [row][wave]: counts, then offsets
     __shared__ int32_t st_idx[kStage];
     __shared__ float st_p[kStage];
     __shared__ float msum[kSelWaves];
@@ -203,14 +206,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
     float psum = 0.f;
     bool done = false;  // uniform
 
-    if (k < n && E <= kSelPerThread) {
+    if (k < n && E <= PT) {
         // ---- fast path: column j = e * 1024 + tid in v[e]; the slots past n first hold
         //      copies of column n - 1 (no change to the extremes), then -inf, which no bin
         //      counts and no threshold takes ----
         const float kNegInf = -__builtin_huge_valf();
-        float v[kSelPerThread];
+        float v[PT];
 #pragma unroll
-        for (int e = 0; e < kSelPerThread; ++e) v[e] = sc[min(e * kSelThreads + tid, n - 1)];
+        for (int e = 0; e < PT; ++e) v[e] = sc[min(e * kSelThreads + tid, n - 1)];
         for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
         for (int i = tid; i < kCandCap; i += kSelThreads) cand[i] = 0;  // padding ranks below everything
         // -inf scores (masked columns) take no bin and are never taken here; the k-th score
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
         float mn = __builtin_huge_valf(), mx = kNegInf;
         float vsum = 0.f;  // NaN iff some score is NaN (or +inf and -inf meet: not finite either)
 #pragma unroll
-        for (int e = 0; e < kSelPerThread; ++e) {
+        for (int e = 0; e < PT; ++e) {
             mn = fminf(mn, v[e] == kNegInf ? __builtin_huge_valf() : v[e]);
             mx = fmaxf(mx, v[e]);
             vsum += v[e];
@@ -234,10 +237,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
         if (tid == 0) {
             bcast[0] = kNoBin;  // stays so only if the histogram misses the k-th column
             bcast[2] = 0;       // candidate count
-            thr_unique = 0u;    // stays 0 unless the ranking finds the threshold column
+            thr_found = 0u;     // 1: the threshold column found, its score unique; 2: found, shared
         }
 #pragma unroll
-        for (int e = 0; e < kSelPerThread; ++e) v[e] = e * kSelThreads + tid < n ? v[e] : kNegInf;
+        for (int e = 0; e < PT; ++e) v[e] = e * kSelThreads + tid < n ? v[e] : kNegInf;
         __syncthreads();
         float lo = fmin_sh[0], hi = fmax_sh[0];
 #pragma unroll
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
         const float scale = (float)kBins / range;
         if (range > 0.f && __builtin_isfinite(range) && __builtin_isfinite(scale)) {
 #pragma unroll
-            for (int e = 0; e < kSelPerThread; ++e)
+            for (int e = 0; e < PT; ++e)
                 if (v[e] > kNegInf) atomicAdd(&hist[value_bin(v[e], lo, scale)], 1u);
             __syncthreads();
             // bin of the k-th largest, counting from the top bin (thread t: bins 2047-2t, 2046-2t)
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
             if (bcast[0] != kNoBin && hist[bstar] <= (uint32_t)kCandCap) {
                 // the threshold bin's columns as (key, index) sort words
 #pragma unroll
-                for (int e = 0; e < kSelPerThread; ++e) {
+                for (int e = 0; e < PT; ++e) {
                     if (value_bin(v[e], lo, scale) == bstar) {  // never for -inf (bin -1)
                         const uint32_t slot = atomicAdd(&bcast[2], 1u);
                         cand[slot] = sort_word(v[e], e * kSelThreads + tid);
@@ -280,8 +283,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
                 }
                 __syncthreads();
                 // the candidate of rank need_in - 1 (bins are monotone in the score, so every
-                // column of a higher bin precedes it and every column of a lower bin follows),
-                // and whether any other column has its score
+                // column of a higher bin precedes it and every column of a lower bin follows)
                 const uint32_t c = bcast[2];
                 const uint32_t cpad = (c + 7u) & ~7u;
                 for (uint32_t t = tid; t < c; t += kSelThreads) {
@@ -298,19 +300,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
                     }
                     if (rank == need_in - 1) {
                         thr_sh = rt;
-                        thr_unique = same == 1u;
+                        thr_found = same == 1u ? 1u : 2u;
                     }
                 }
                 __syncthreads();
-                if (thr_unique) {
-                    // a unique threshold score tx: a column is taken iff its score is >= tx
-                    // (columns past n hold -inf); per-(row, wave) counts (lane e of cnts: row
-                    // e), one scan, then each column's position
+                // the threshold word (tx, jt): a column is taken iff its word is at least that,
+                // i.e. its score is above tx, or equal to it (+0 and -0 alike) at an index up
+                // to jt; when no other column has the score tx (TIE false) that is just a
+                // score of at least tx (columns past n hold -inf).  Per-(row, wave) counts
+                // (lane e of cnts: row e), one scan, then each column's position.
+                auto compact = [&](auto tiec) {
+                    constexpr bool TIE = decltype(tiec)::value;
                     const float tx = key_float((uint32_t)(thr_sh >> 32));
+                    const int jt = (int)~(uint32_t)thr_sh;
                     uint32_t cnts = 0;
 #pragma unroll
-                    for (int e = 0; e < kSelPerThread; ++e) {
-                        const uint32_t cnt = (uint32_t)__popcll(__ballot(v[e] >= tx));
+                    for (int e = 0; e < PT; ++e) {
+                        const bool f = TIE ? v[e] > tx || (v[e] == tx && e * kSelThreads + tid <= jt) : v[e] >= tx;
+                        const uint32_t cnt = (uint32_t)__popcll(__ballot(f));
                         cnts = lane == e ? cnt : cnts;
                     }
                     if (lane < E) row_off[lane * kSelWaves + wave] = cnts;
@@ -329,8 +336,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
                     float txp = tx;
                     asm volatile("" : "+v"(txp));
 #pragma unroll
-                    for (int e = 0; e < kSelPerThread; ++e) {
-                        const bool f = v[e] >= txp;
+                    for (int e = 0; e < PT; ++e) {
+                        const bool f = TIE ? v[e] > txp || (v[e] == txp && e * kSelThreads + tid <= jt) : v[e] >= txp;
                         const uint64_t bal = __ballot(f);
                         const uint32_t base = __builtin_amdgcn_readlane(offs, e);
                         if (f) {
@@ -359,7 +366,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
                         }
                     }
                     done = true;
-                }
+                };
+                if (thr_found == 1u) compact(std::false_type{});
+                else if (thr_found == 2u) compact(std::true_type{});
             }
         }
         __syncthreads();
@@ -386,7 +395,15 @@ size_t select_ws_bytes(int, int, int) { return 0; }
 
 int launch_select(const float* scores, int ld, const float* lse, int B, int H, int n, int k, int32_t* idx,
                   float* p_sel, float* mass, void*, hipStream_t st) {
-    select_kernel<<<B * H, kSelThreads, 0, st>>>(scores, ld, lse, n, k, idx, p_sel, mass);
+    // the fewest register-resident scores per thread that hold the row (longer rows take the
+    // memory paths from the largest)
+    const int E = (n + kSelThreads - 1) / kSelThreads;
+    if (E <= 10)
+        select_kernel<10><<<B * H, kSelThreads, 0, st>>>(scores, ld, lse, n, k, idx, p_sel, mass);
+    else if (E <= 20)
+        select_kernel<20><<<B * H, kSelThreads, 0, st>>>(scores, ld, lse, n, k, idx, p_sel, mass);
+    else
+        select_kernel<kSelPerThread><<<B * H, kSelThreads, 0, st>>>(scores, ld, lse, n, k, idx, p_sel, mass);
     return hipGetLastError() == hipSuccess ? QKV_OK : QKV_ELAUNCH;
 }
 
