@@ -7,7 +7,8 @@
 // (up to PT of them: 10, 20 or 40, the fewest that hold the row) in registers.  A histogram
 // over 2048 equal-width value bins between the smallest and largest score finds the bin
 // holding the k-th column (bins are a monotone function of the score, so every bin above it
-// is taken whole); the few columns of that bin are ranked exactly as 64-bit (key, index)
+// is taken whole; a bin of more than 256 columns is split again by a second histogram over its
+// own [min, max]); the few columns of that bin are ranked exactly as 64-bit (key, index)
 // words, which gives the threshold word (x_t, j_t).  A column is taken iff its score is above
 // x_t, or equal to it at an index up to j_t: ties across the threshold are decided here too.
 // One scan over per-(row, wave) counts places the selected columns in ascending index order.
@@ -28,6 +29,7 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelPerThread = 40;      // register-resident scores per thread at most (n <= 40960)
 constexpr int kBins = 2048;
 constexpr int kCandCap = 2048;         // threshold-bin columns ranked exactly
+constexpr int kRefine = 256;           // threshold bins above this size get a second histogram
 constexpr int kStage = 4096;           // selections staged in LDS for coalesced stores
 constexpr uint32_t kNoBin = 0xFFFFFFFFu;  // no threshold bin found
 
@@ -54,6 +56,13 @@ __device__ __forceinline__ uint64_t sort_word(float x, int j) {
 // Rounding is monotone, so the bin is monotone in x, which is all the selection needs of it.
 __device__ __forceinline__ int value_bin(float x, float lo, float scale) {
     return (int)__builtin_amdgcn_fmed3f((x - lo) * scale, -1.f, (float)(kBins - 1));
+}
+
+// Bin of a score x >= lo from its order key (monotone: the key is, and so are the unsigned
+// difference, its rounding to fp32 and the product); -inf gets bin -1.
+__device__ __forceinline__ int key_bin(float x, uint32_t klo, float scale) {
+    if (x == -__builtin_huge_valf()) return -1;
+    return (int)__builtin_amdgcn_fmed3f((float)(order_key(x) - klo) * scale, -1.f, (float)(kBins - 1));
 }
 
 __device__ __forceinline__ uint64_t lanes_below() {
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t scan_sh[kSelWaves];
     __shared__ float fmin_sh[kSelWaves], fmax_sh[kSelWaves];
-    __shared__ uint32_t bcast[4];
+    __shared__ uint32_t bcast[6];
     __shared__ uint64_t cand[kCandCap];
     __shared__ uint64_t thr_sh;
     __shared__ uint32_t thr_found;
@@ -249,11 +258,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
             hi = fmaxf(hi, fmax_sh[w]);
         }
         const float range = hi - lo;
-        const float scale = (float)kBins / range;
+        // First-level bins: of the score over [lo, hi], or (kmode), for rows whose finite scores
+        // are all >= 0 and span more than a factor of 64, of its order key over [key(lo),
+        // key(hi)], which is close to log2 of the score: heavy-tailed rows (token-change ratios)
+        // then spread over the bins instead of piling into the lowest few.  The mode is uniform,
+        // so each loop that bins comes in two forms rather than testing it per column.
+        const bool kmode = lo >= 0.f && hi > 64.f * lo;
+        const uint32_t klo = order_key(lo);
+        const float scale = kmode ? (float)kBins / (float)(order_key(hi) - klo) : (float)kBins / range;
         if (range > 0.f && __builtin_isfinite(range) && __builtin_isfinite(scale)) {
+            if (kmode) {
 #pragma unroll
-            for (int e = 0; e < PT; ++e)
-                if (v[e] > kNegInf) atomicAdd(&hist[value_bin(v[e], lo, scale)], 1u);
+                for (int e = 0; e < PT; ++e)
+                    if (v[e] > kNegInf) atomicAdd(&hist[key_bin(v[e], klo, scale)], 1u);
+            } else {
+#pragma unroll
+                for (int e = 0; e < PT; ++e)
+                    if (v[e] > kNegInf) atomicAdd(&hist[value_bin(v[e], lo, scale)], 1u);
+            }
             __syncthreads();
             // bin of the k-th largest, counting from the top bin (thread t: bins 2047-2t, 2046-2t)
             const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
@@ -269,16 +291,108 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
             }
             __syncthreads();
             const int bstar = (int)bcast[0];
-            const uint32_t need_in = (uint32_t)k - bcast[1];  // columns taken inside the threshold bin
+            uint32_t need_in = (uint32_t)k - bcast[1];  // columns taken inside the threshold bin
             // every column of the fast path is finite and binned, so the k-th is always found;
             // should it not be, the memory paths decide
-            if (bcast[0] != kNoBin && hist[bstar] <= (uint32_t)kCandCap) {
-                // the threshold bin's columns as (key, index) sort words
+            bool ok = bcast[0] != kNoBin;
+            const uint32_t cb = ok ? hist[bstar] : 0u;
+            // A crowded threshold bin (heavy-tailed scores put most columns in the lowest bins
+            // of [min, max]) is split once more, by a second histogram over the bin's own
+            // [min, max]; the bin of the k-th column there holds the candidates.  Without it
+            // the exact ranking costs (bin size)^2 comparisons.
+            int sb = -1;
+            float lo2 = 0.f, scale2 = 0.f;
+            if (ok && cb > (uint32_t)kRefine) {
+                float mn2 = __builtin_huge_valf(), mx2 = kNegInf;
+                if (kmode) {
 #pragma unroll
-                for (int e = 0; e < PT; ++e) {
-                    if (value_bin(v[e], lo, scale) == bstar) {  // never for -inf (bin -1)
-                        const uint32_t slot = atomicAdd(&bcast[2], 1u);
-                        cand[slot] = sort_word(v[e], e * kSelThreads + tid);
+                    for (int e = 0; e < PT; ++e) {
+                        if (key_bin(v[e], klo, scale) == bstar) {
+                            mn2 = fminf(mn2, v[e]);
+                            mx2 = fmaxf(mx2, v[e]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < PT; ++e) {
+                        if (value_bin(v[e], lo, scale) == bstar) {
+                            mn2 = fminf(mn2, v[e]);
+                            mx2 = fmaxf(mx2, v[e]);
+                        }
+                    }
+                }
+                mn2 = wave_min(mn2);
+                mx2 = wave_max(mx2);
+                __syncthreads();  // every thread has read the first level's extremes and counts
+                if (lane == 0) {
+                    fmin_sh[wave] = mn2;
+                    fmax_sh[wave] = mx2;
+                }
+                for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
+                if (tid == 0) bcast[3] = kNoBin;
+                __syncthreads();
+                lo2 = fmin_sh[0];
+                float hi2 = fmax_sh[0];
+#pragma unroll
+                for (int w = 1; w < kSelWaves; ++w) {
+                    lo2 = fminf(lo2, fmin_sh[w]);
+                    hi2 = fmaxf(hi2, fmax_sh[w]);
+                }
+                const float range2 = hi2 - lo2;
+                scale2 = (float)kBins / range2;
+                if (range2 > 0.f && __builtin_isfinite(scale2)) {
+                    if (kmode) {
+#pragma unroll
+                        for (int e = 0; e < PT; ++e)
+                            if (key_bin(v[e], klo, scale) == bstar) atomicAdd(&hist[value_bin(v[e], lo2, scale2)], 1u);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < PT; ++e)
+                            if (value_bin(v[e], lo, scale) == bstar) atomicAdd(&hist[value_bin(v[e], lo2, scale2)], 1u);
+                    }
+                    __syncthreads();
+                    const int s0 = kBins - 1 - 2 * tid, s1 = s0 - 1;
+                    const uint32_t d0 = hist[s0], d1 = hist[s1];
+                    uint32_t tot2;
+                    const uint32_t above2 = block_excl_scan(d0 + d1, scan_sh, &tot2);
+                    if (above2 < need_in && need_in <= above2 + d0) {
+                        bcast[3] = (uint32_t)s0;
+                        bcast[4] = above2;
+                    } else if (above2 + d0 < need_in && need_in <= above2 + d0 + d1) {
+                        bcast[3] = (uint32_t)s1;
+                        bcast[4] = above2 + d0;
+                    }
+                    __syncthreads();
+                    ok = bcast[3] != kNoBin;
+                    if (ok) {
+                        sb = (int)bcast[3];
+                        need_in -= bcast[4];
+                        ok = hist[sb] <= (uint32_t)kCandCap;
+                    }
+                } else {
+                    ok = cb <= (uint32_t)kCandCap;  // one score throughout the bin: all tie
+                }
+            } else {
+                ok = ok && cb <= (uint32_t)kCandCap;
+            }
+            if (ok) {
+                // the threshold (sub)bin's columns as (key, index) sort words
+                // (never for -inf: bin -1)
+                if (kmode) {
+#pragma unroll
+                    for (int e = 0; e < PT; ++e) {
+                        if (key_bin(v[e], klo, scale) == bstar && (sb < 0 || value_bin(v[e], lo2, scale2) == sb)) {
+                            const uint32_t slot = atomicAdd(&bcast[2], 1u);
+                            cand[slot] = sort_word(v[e], e * kSelThreads + tid);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < PT; ++e) {
+                        if (value_bin(v[e], lo, scale) == bstar && (sb < 0 || value_bin(v[e], lo2, scale2) == sb)) {
+                            const uint32_t slot = atomicAdd(&bcast[2], 1u);
+                            cand[slot] = sort_word(v[e], e * kSelThreads + tid);
+                        }
                     }
                 }
                 __syncthreads();
