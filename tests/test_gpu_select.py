@@ -131,3 +131,26 @@ def test_skewed_rows(n):
     for k in (1, -(-n // 10), n // 4, n // 4 + 2, n // 2, n - 1):
         say(f"  select skewed rows n={n} k={k}")
         run_case(S, lse, k)
+
+
+@pytest.mark.parametrize("n", [4097, 32768])
+def test_nonnegative_wide_rows(n):
+    # rows whose finite scores are all >= 0 and span many binades (binned by order key): with
+    # exact zeros and -0.0 among them (equal to +0), values from 1e-30 to 1e30, a row of
+    # half-normal scores, and ties planted at the k-th score
+    g = np.random.default_rng(n + 31)
+    S = np.zeros((1, 4, n), np.float32)
+    S[0, 0] = np.abs(g.standard_normal(n)).astype(np.float32)
+    S[0, 0, ::9] = 0.0
+    S[0, 0, 4::9] = -0.0
+    S[0, 1] = (10.0 ** g.uniform(-30, 30, n)).astype(np.float32)
+    S[0, 2] = np.exp(2.0 * g.standard_normal(n)).astype(np.float32)
+    S[0, 2, ::11] = -np.inf
+    S[0, 3] = np.round(np.exp(g.standard_normal(n)) * 8) / 8          # coarse: many ties
+    srt = np.sort(S[0, 2][np.isfinite(S[0, 2])])[::-1]
+    S[0, 2, g.choice(n, 4, replace=False)] = srt[n // 4 - 1]
+    mx = S.max(-1, keepdims=True).astype(np.float64)
+    lse = (np.log(np.exp(S.astype(np.float64) - mx).sum(-1)) + mx[..., 0]).astype(np.float32)
+    for k in (1, -(-n // 10), n // 4, n // 4 + 1, n // 2, n - 1):
+        say(f"  select non-negative wide rows n={n} k={k}")
+        run_case(S, lse, k)
