@@ -14,7 +14,8 @@ namespace qkv {
 
 constexpr int kTokWaves = 4;
 
-// score[b][t] = -inf for every token; the zero lse the selector is given
+// score[b][t] = -inf for every token; the zero lse the selector is given (only needed when
+// the preceding set is a list: with every token scored, the score kernel writes the lse)
 __global__ __launch_bounds__(256) void token_fill_kernel(float* __restrict__ score, int n, float* __restrict__ zlse) {
     const int b = blockIdx.y;
     const int t = blockIdx.x * 256 + threadIdx.x;
@@ -28,9 +29,10 @@ __global__ __launch_bounds__(64 * kTokWaves) void token_score_kernel(const uint1
                                                                      const uint16_t* __restrict__ hp, int ld_tok,
                                                                      int n, int dm, const int32_t* __restrict__ act,
                                                                      const int32_t* __restrict__ n_act, int ld_act,
-                                                                     float* __restrict__ score) {
+                                                                     float* __restrict__ score, float* __restrict__ zlse) {
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
+    if (zlse && blockIdx.x == 0 && threadIdx.x == 0) zlse[b] = 0.f;
     const int i = blockIdx.x * kTokWaves + (threadIdx.x >> 6);
     int t;
     if (act) {
@@ -63,9 +65,12 @@ __global__ __launch_bounds__(64 * kTokWaves) void token_score_kernel(const uint1
 
 // Drops the selected entries whose score is -inf (tokens outside the preceding set, picked
 // only when k exceeds its size), in place and in order; writes the count and the count of
-// positions below `split`.  One workgroup of kCompactWaves waves per sequence.
+// positions below `split`.  One workgroup of kCompactWaves waves per sequence; each pass
+// reads kCompactPer chunks of entries and their scores with all loads in flight, then
+// places the chunks one after another.
 constexpr int kCompactWaves = 16;
 constexpr int kCompactThreads = 64 * kCompactWaves;
+constexpr int kCompactPer = 8;
 
 __global__ __launch_bounds__(kCompactThreads) void token_compact_kernel(const float* __restrict__ score, int n, int k,
                                                                         int32_t* __restrict__ act_out,
@@ -75,30 +80,44 @@ __global__ __launch_bounds__(kCompactThreads) void token_compact_kernel(const fl
     int32_t* a = act_out + (size_t)b * k;
     __shared__ uint32_t wcnt[kCompactWaves], wlow[kCompactWaves];
     uint32_t base = 0, below = 0;
-    for (int i0 = 0; i0 < k; i0 += kCompactThreads) {
-        const int i = i0 + tid;
-        const int t = i < k ? a[i] : -1;
-        const bool keep = t >= 0 && t < n && score[(size_t)b * n + t] > -__builtin_huge_valf();
-        const uint64_t bal = __ballot(keep);
-        // positions below the split: the kept entries are ascending
-        const uint64_t bs = __ballot(keep && t < split);
-        if (lane == 0) {
-            wcnt[wave] = (uint32_t)__popcll(bal);
-            wlow[wave] = (uint32_t)__popcll(bs);
-        }
-        __syncthreads();  // every entry of this chunk has been read
-        uint32_t before = 0, all = 0, low = 0;
+    const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    for (int p0 = 0; p0 < k; p0 += kCompactThreads * kCompactPer) {
+        int t[kCompactPer];
+        bool keep[kCompactPer];
 #pragma unroll
-        for (int w = 0; w < kCompactWaves; ++w) {
-            before += w < wave ? wcnt[w] : 0u;
-            all += wcnt[w];
-            low += wlow[w];
+        for (int e = 0; e < kCompactPer; ++e) {
+            const int i = p0 + e * kCompactThreads + tid;
+            t[e] = i < k ? a[i] : -1;
         }
-        const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-        if (keep) a[base + before + (uint32_t)__popcll(bal & lower)] = t;  // never past entry i
-        below += low;
-        base += all;
-        __syncthreads();  // the counts are read before the next chunk writes them
+        // (every entry read here is complete before the first barrier below: its score load,
+        // issued before it, needs the entry as its address)
+#pragma unroll
+        for (int e = 0; e < kCompactPer; ++e)
+            keep[e] = t[e] >= 0 && t[e] < n && score[(size_t)b * n + t[e]] > -__builtin_huge_valf();
+#pragma unroll
+        for (int e = 0; e < kCompactPer; ++e) {
+            if (p0 + e * kCompactThreads >= k) break;   // uniform
+            const uint64_t bal = __ballot(keep[e]);
+            // positions below the split: the kept entries are ascending
+            const uint64_t bs = __ballot(keep[e] && t[e] < split);
+            if (lane == 0) {
+                wcnt[wave] = (uint32_t)__popcll(bal);
+                wlow[wave] = (uint32_t)__popcll(bs);
+            }
+            // every entry of this pass has been read (chunk 0), the counts are written
+            __syncthreads();
+            uint32_t before = 0, all = 0, low = 0;
+#pragma unroll
+            for (int w = 0; w < kCompactWaves; ++w) {
+                before += w < wave ? wcnt[w] : 0u;
+                all += wcnt[w];
+                low += wlow[w];
+            }
+            if (keep[e]) a[base + before + (uint32_t)__popcll(bal & lower)] = t[e];  // never past its entry
+            below += low;
+            base += all;
+            __syncthreads();  // the counts are read before the next chunk writes them
+        }
     }
     if (tid == 0) {
         n_out[b] = (int32_t)base;
@@ -114,10 +133,11 @@ int launch_select_tokens(const uint16_t* hc, const uint16_t* hp, int ld_tok, int
     float* zlse = static_cast<float*>(ws);
     float* mass = zlse + B;
     float* p_sel = mass + B;
-    token_fill_kernel<<<dim3((n + 255) / 256, B), 256, 0, st>>>(score, n, zlse);
+    // with every token scored, every score is written: no fill
+    if (act) token_fill_kernel<<<dim3((n + 255) / 256, B), 256, 0, st>>>(score, n, zlse);
     const int rows = act ? ld_act : n;
     token_score_kernel<<<dim3((rows + kTokWaves - 1) / kTokWaves, B), 64 * kTokWaves, 0, st>>>(
-        hc, hp, ld_tok, n, dm, act, n_act, ld_act, score);
+        hc, hp, ld_tok, n, dm, act, n_act, ld_act, score, act ? nullptr : zlse);
     if (hipGetLastError() != hipSuccess) return QKV_ELAUNCH;
     const int rc = launch_select(score, n, zlse, B, 1, n, k, act_out, p_sel, mass, nullptr, st);
     if (rc != QKV_OK) return rc;

@@ -88,6 +88,12 @@ def test_nested_selection_loops_3_and_4(n, dm, B):
                                                         ((0, 0), (0, 0))), m4.sum(1))
     for b in range(B):
         assert np.array_equal(g5[1][b, :g5[2][b]], np.nonzero(m4[b])[0])
+    # the same over more than one compaction pass (8192 entries each): k above loop 3's set
+    k6 = min(n, k3 + 8192 + 7)
+    g6 = run_select(H[3], H[2], n, k6, ap, m3.sum(1), split=n // 3)
+    for b in range(B):
+        assert np.array_equal(g6[1][b, :g6[2][b]], np.nonzero(m3[b])[0])
+        assert g6[3][b] == int(np.sum(np.nonzero(m3[b])[0] < n // 3)), "count below the split"
 
 
 def test_ties_and_zero_states():
