@@ -90,6 +90,19 @@ def test_deep_recurrence_32_loops():
     check_step(p, p.queries(0), w.n_dense, w.k_cols(900), "R=32")
 
 
+@pytest.mark.parametrize("codec", [{}, {"full_state": True}, {"residual_bits": 2}], ids=["int4", "full", "int2"])
+def test_deep_recurrence_head_dim_64(codec):
+    # d = 64: the deep-chain gather's long columns then spread over eight lane groups of 8
+    # lanes (rather than four of 16), with a step across the 64-row tail flush
+    w = dataclasses.replace(W["deep32"], H=2, d=64)
+    p = Pair(w, n=900, extra=70, **codec)
+    compare_planes(p.gpu, p.orc, range(2), range(2), loops=[0, 1, 2, 31])
+    check_step(p, p.queries(0), w.n_dense, w.k_cols(900), f"R=32 d=64 {codec}")
+    for step in range(66):
+        p.append(step)
+    check_step(p, p.queries(1), w.n_dense, w.k_cols(p.gpu.n_ctx), f"R=32 d=64 {codec} after a flush")
+
+
 def test_deep_chain_stored_loops_mask():
     # the per-position mask of the loops whose sparse planes store a position matches the
     # planes' contents, and the deep-chain gather gives the same bits with and without it
