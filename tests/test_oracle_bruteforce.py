@@ -1,0 +1,196 @@
+"""An independent numpy brute force of the whole method on the tiny workload, compared with
+the oracle.
+
+It is written from the definitions on the pages (project page STEP 01 to STEP 03; explainer
+section 3: per-loop residual INT4 of the active tokens against the preceding loop's
+reconstruction, keys per channel over 64 stored tokens, values per token over 64 channels,
+asymmetric; the BF16 tail of the most recent tokens; dense early loops; top-K columns from the
+preceding loop with the cached mass and the rank-K splice), in numpy, without any of the
+oracle's code.  The fused multiply-add of the dequantisation is emulated exactly.
+
+Checked against the oracle: every loop's reconstruction of keys and values bit for bit, after
+the prefill and after 64 generated tokens (one 64-row flush of every loop); then a decode step
+of all four loops: outputs, scores and lse in fp64 up to summation order, the selected columns
+exactly, their probabilities and mass.
+"""
+import numpy as np
+import pytest
+
+from quantized_kv_attention_amd import synth
+
+F32 = np.float32
+
+
+def widen(u16):
+    return (np.asarray(u16, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def fmaf32(c, s, z):
+    """fp32 fma(c, s, z), rounded once: c * s is exact in fp64 (c <= 15), the sum carries
+    its rounding error e (two-sum), and e breaks the one case fp64 cannot: a sum exactly
+    halfway between two fp32 values."""
+    p = np.asarray(c, np.float64) * np.asarray(s, np.float32).astype(np.float64)
+    zz = np.asarray(z, np.float32).astype(np.float64)
+    t = p + zz
+    bp = t - zz
+    e = (p - bp) + (zz - (t - bp))
+    r = t.astype(np.float32)
+    up = np.nextafter(r, F32(np.inf))
+    dn = np.nextafter(r, F32(-np.inf))
+    at_up = t == (r.astype(np.float64) + up.astype(np.float64)) / 2
+    at_dn = t == (r.astype(np.float64) + dn.astype(np.float64)) / 2
+    r = np.where(at_up & (e > 0), up, r)
+    return np.where(at_dn & (e < 0), dn, r).astype(np.float32)
+
+
+def quantize(x):
+    """One group: s = (max - min) / 15, z = min (+0 for -0), codes rint((x - z) / s) in [0, 15]
+    (0 where s is 0), all in fp32; returns the dequantised values."""
+    x = np.asarray(x, np.float32)
+    mn, mx = x.min(), x.max()
+    s = F32(F32(mx - mn) / F32(15))
+    z = F32(mn + F32(0))
+    if s == 0:
+        codes = np.zeros(x.shape)
+    else:
+        codes = np.clip(np.rint((x - z) / s), 0, 15)
+    return fmaf32(codes, np.full(x.shape, s, np.float32), np.full(x.shape, z, np.float32))
+
+
+def encode_call(Xin, Xhat, act, r, p0, p1):
+    """Encode loop r (0-based) over positions [p0, p1) of one head: Xin[r], Xhat[r] [n, d]."""
+    rows = p0 + np.nonzero(act[r][p0:p1])[0]
+    if r > 0:
+        Xhat[r][p0:p1] = Xhat[r - 1][p0:p1]          # inactive rows keep loop r-1
+    if rows.size == 0:
+        return
+    X = Xin[r][rows]
+    D = X if r == 0 else (X - Xhat[r - 1][rows]).astype(np.float32)
+    return rows, D
+
+
+def encode(Kin, Vin, Khat, Vhat, act, p0, p1, R):
+    for r in range(R):
+        for Xin, Xhat, key in ((Kin, Khat, True), (Vin, Vhat, False)):
+            got = encode_call(Xin, Xhat, act, r, p0, p1)
+            if got is None:
+                continue
+            rows, D = got
+            deq = np.zeros_like(D)
+            if key:   # per channel, over groups of 64 consecutive stored rows of this call
+                for g0 in range(0, rows.size, 64):
+                    for c in range(D.shape[1]):
+                        deq[g0:g0 + 64, c] = quantize(D[g0:g0 + 64, c])
+            else:     # per stored row, over groups of 64 channels
+                for i in range(rows.size):
+                    for c0 in range(0, D.shape[1], 64):
+                        deq[i, c0:c0 + 64] = quantize(D[i, c0:c0 + 64])
+            Xhat[r][rows] = deq if r == 0 else (Xhat[r - 1][rows] + deq).astype(np.float32)
+
+
+def set_tail(Kin, Vin, Khat, Vhat, act, p0, p1, R):
+    for r in range(R):
+        for Xin, Xhat in ((Kin, Khat), (Vin, Vhat)):
+            a = act[r][p0:p1, None]
+            prev = Xin[r][p0:p1] if r == 0 else Xhat[r - 1][p0:p1]
+            Xhat[r][p0:p1] = np.where(a, Xin[r][p0:p1], prev)
+
+
+def body(n):
+    return 64 * ((n - 64) // 64) if n >= 64 else 0
+
+
+def step(q, Khat, Vhat, n, n_dense, k, R):
+    """One decode step of every loop for one head (sm = 1: the queries carry 1/sqrt(d)).
+    Dense loops attend to every column; a sparse loop selects the top k of the preceding
+    loop's scores (as fp32, with its lse as fp32), keeps their mass and splices the new
+    in-set softmax into the preceding output and scores."""
+    out = []
+    scores = lse = o_prev = None
+    for r in range(R):
+        qf = widen(q[r]).astype(np.float64)
+        Kr, Vr = Khat[r][:n].astype(np.float64), Vhat[r][:n].astype(np.float64)
+        if r < n_dense:
+            scores = Kr @ qf
+            mx = scores.max()
+            lse = mx + np.log(np.exp(scores - mx).sum())
+            o = (np.exp(scores - lse)[:, None] * Vr).sum(0)
+            out.append(dict(o=o, scores=scores.copy(), lse=lse))
+        else:
+            s32, lse32 = scores.astype(np.float32), np.float64(F32(lse))
+            order = np.lexsort((np.arange(n), -s32.astype(np.float64)))   # score down, index up
+            idx = np.sort(order[:k])
+            p = np.exp(s32[idx].astype(np.float64) - lse32)
+            m = p.sum()
+            sn = Kr[idx] @ qf
+            mx = sn.max()
+            lse_s = mx + np.log(np.exp(sn - mx).sum())
+            alpha = np.exp(sn - lse_s)
+            Vp = Vhat[r - 1][:n].astype(np.float64)
+            o = o_prev + (m * alpha[:, None] * Vr[idx]).sum(0) - (p[:, None] * Vp[idx]).sum(0)
+            scores = scores.copy()
+            scores[idx] = lse32 + np.log(m) + sn - lse_s
+            lse = lse32
+            out.append(dict(o=o, scores=scores.copy(), lse=lse, idx=idx, p_sel=p, mass=m))
+        o_prev = o
+    return out
+
+
+def test_brute_force_matches_oracle(orc):
+    w = synth.WORKLOADS["tiny"]
+    K, V, act = synth.gen_layer(w)
+    n0, cap = w.n, w.n + 80
+    oc = orc.OracleCache(w.B, w.H, w.d, w.R, cap=cap)
+    oc.prefill(K, V, act)
+
+    # the brute force's own state for (sequence 0, head 0)
+    Kin = [np.zeros((cap, w.d), np.float32) for _ in range(w.R)]
+    Vin = [np.zeros((cap, w.d), np.float32) for _ in range(w.R)]
+    Khat = [np.zeros((cap, w.d), np.float32) for _ in range(w.R)]
+    Vhat = [np.zeros((cap, w.d), np.float32) for _ in range(w.R)]
+    A = [np.zeros(cap, bool) for _ in range(w.R)]
+    for r in range(w.R):
+        Kin[r][:n0], Vin[r][:n0] = widen(K[r][0, 0]), widen(V[r][0, 0])
+        A[r][:n0] = act[r][0]
+    nb = body(n0)
+    encode(Kin, Vin, Khat, Vhat, A, 0, nb, w.R)
+    set_tail(Kin, Vin, Khat, Vhat, A, nb, n0, w.R)
+
+    def same_state(n, label):
+        for r in range(w.R):
+            assert np.array_equal(Khat[r][:n], oc.Khat[r][0, 0, :n]), f"{label}: keys of loop {r + 1}"
+            assert np.array_equal(Vhat[r][:n], oc.Vhat[r][0, 0, :n]), f"{label}: values of loop {r + 1}"
+
+    same_state(n0, "prefill")
+    # 64 generated tokens (active in every loop): the tail reaches 128 once, and its oldest 64
+    # rows are encoded into every loop, loops in order
+    n = n0
+    for t in range(64):
+        kn, vn = synth.gen_new_token(w, t)
+        nb_new = body(n + 1)
+        if nb_new > nb:
+            encode(Kin, Vin, Khat, Vhat, A, nb, nb_new, w.R)
+            nb = nb_new
+        for r in range(w.R):
+            Kin[r][n], Vin[r][n] = widen(kn[r][0, 0]), widen(vn[r][0, 0])
+            A[r][n] = True
+        set_tail(Kin, Vin, Khat, Vhat, A, n, n + 1, w.R)
+        oc.append(kn, vn)
+        n += 1
+    assert nb == n0 and oc.nb == nb
+    same_state(n, "after the flush")
+
+    q = synth.gen_queries(w, 3)
+    k = w.k_cols(n)
+    ref = oc.step(q, w.n_dense, k)
+    got = step([x[0, 0] for x in q], Khat, Vhat, n, w.n_dense, k, w.R)
+    for r in range(w.R):
+        g, o = got[r], ref[r]
+        np.testing.assert_allclose(g["o"], o["o"][0, 0], rtol=1e-11, atol=1e-13, err_msg=f"o, loop {r + 1}")
+        np.testing.assert_allclose(g["scores"], o["scores"][0, 0], rtol=1e-11, atol=1e-11,
+                                   err_msg=f"scores, loop {r + 1}")
+        assert abs(g["lse"] - o["lse"][0, 0]) < 1e-11
+        if r >= w.n_dense:
+            assert np.array_equal(g["idx"], o["idx"][0][0]), f"selection, loop {r + 1}"
+            np.testing.assert_allclose(g["p_sel"], o["p_sel"][0][0], rtol=1e-12)
+            assert g["mass"] == pytest.approx(o["mass"][0, 0], rel=1e-12)
