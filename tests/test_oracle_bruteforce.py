@@ -43,36 +43,40 @@ def fmaf32(c, s, z):
     return np.where(at_dn & (e < 0), dn, r).astype(np.float32)
 
 
-def quantize(x):
-    """One group: s = (max - min) / 15, z = min (+0 for -0), codes rint((x - z) / s) in [0, 15]
-    (0 where s is 0), all in fp32; returns the dequantised values."""
+def quantize(x, top=15):
+    """One group: s = (max - min) / top, z = min (+0 for -0), codes rint((x - z) / s) in
+    [0, top] (0 where s is 0), all in fp32; returns the dequantised values.  top = 15 for
+    4-bit codes, 3 for 2-bit ones."""
     x = np.asarray(x, np.float32)
     mn, mx = x.min(), x.max()
-    s = F32(F32(mx - mn) / F32(15))
+    s = F32(F32(mx - mn) / F32(top))
     z = F32(mn + F32(0))
     if s == 0:
         codes = np.zeros(x.shape)
     else:
-        codes = np.clip(np.rint((x - z) / s), 0, 15)
+        codes = np.clip(np.rint((x - z) / s), 0, top)
     return fmaf32(codes, np.full(x.shape, s, np.float32), np.full(x.shape, z, np.float32))
 
 
-def encode_call(Xin, Xhat, act, r, p0, p1):
-    """Encode loop r (0-based) over positions [p0, p1) of one head: Xin[r], Xhat[r] [n, d]."""
+def encode_call(Xin, Xhat, act, r, p0, p1, full):
+    """Encode loop r (0-based) over positions [p0, p1) of one head: Xin[r], Xhat[r] [n, d].
+    Returns the stored rows and what they quantise: the residual against loop r-1's
+    reconstruction, or (loop 1, and every loop of the full-state codec) the state itself."""
     rows = p0 + np.nonzero(act[r][p0:p1])[0]
     if r > 0:
         Xhat[r][p0:p1] = Xhat[r - 1][p0:p1]          # inactive rows keep loop r-1
     if rows.size == 0:
         return
     X = Xin[r][rows]
-    D = X if r == 0 else (X - Xhat[r - 1][rows]).astype(np.float32)
+    D = X if (r == 0 or full) else (X - Xhat[r - 1][rows]).astype(np.float32)
     return rows, D
 
 
-def encode(Kin, Vin, Khat, Vhat, act, p0, p1, R):
+def encode(Kin, Vin, Khat, Vhat, act, p0, p1, R, rbits=4, full=False):
     for r in range(R):
+        top = 15 if (r == 0 or full or rbits == 4) else 3
         for Xin, Xhat, key in ((Kin, Khat, True), (Vin, Vhat, False)):
-            got = encode_call(Xin, Xhat, act, r, p0, p1)
+            got = encode_call(Xin, Xhat, act, r, p0, p1, full)
             if got is None:
                 continue
             rows, D = got
@@ -80,12 +84,13 @@ def encode(Kin, Vin, Khat, Vhat, act, p0, p1, R):
             if key:   # per channel, over groups of 64 consecutive stored rows of this call
                 for g0 in range(0, rows.size, 64):
                     for c in range(D.shape[1]):
-                        deq[g0:g0 + 64, c] = quantize(D[g0:g0 + 64, c])
+                        deq[g0:g0 + 64, c] = quantize(D[g0:g0 + 64, c], top)
             else:     # per stored row, over groups of 64 channels
                 for i in range(rows.size):
                     for c0 in range(0, D.shape[1], 64):
-                        deq[i, c0:c0 + 64] = quantize(D[i, c0:c0 + 64])
-            Xhat[r][rows] = deq if r == 0 else (Xhat[r - 1][rows] + deq).astype(np.float32)
+                        deq[i, c0:c0 + 64] = quantize(D[i, c0:c0 + 64], top)
+            chain = r > 0 and not full
+            Xhat[r][rows] = (Xhat[r - 1][rows] + deq).astype(np.float32) if chain else deq
 
 
 def set_tail(Kin, Vin, Khat, Vhat, act, p0, p1, R):
@@ -136,12 +141,16 @@ def step(q, Khat, Vhat, n, n_dense, k, R):
     return out
 
 
-def test_brute_force_matches_oracle(orc):
+@pytest.mark.parametrize("codec", [{}, {"residual_bits": 2}, {"full_state": True}], ids=["int4", "int2", "full"])
+def test_brute_force_matches_oracle(orc, codec):
+    # the codecs: 4-bit residual planes; 2-bit residual planes after the 4-bit base; every
+    # loop its own 4-bit state (the per-loop KIVI ablation)
     w = synth.WORKLOADS["tiny"]
     K, V, act = synth.gen_layer(w)
     n0, cap = w.n, w.n + 80
-    oc = orc.OracleCache(w.B, w.H, w.d, w.R, cap=cap)
+    oc = orc.OracleCache(w.B, w.H, w.d, w.R, cap=cap, **codec)
     oc.prefill(K, V, act)
+    rbits, full = codec.get("residual_bits", 4), codec.get("full_state", False)
 
     # the brute force's own state for (sequence 0, head 0)
     Kin = [np.zeros((cap, w.d), np.float32) for _ in range(w.R)]
@@ -153,7 +162,7 @@ def test_brute_force_matches_oracle(orc):
         Kin[r][:n0], Vin[r][:n0] = widen(K[r][0, 0]), widen(V[r][0, 0])
         A[r][:n0] = act[r][0]
     nb = body(n0)
-    encode(Kin, Vin, Khat, Vhat, A, 0, nb, w.R)
+    encode(Kin, Vin, Khat, Vhat, A, 0, nb, w.R, rbits, full)
     set_tail(Kin, Vin, Khat, Vhat, A, nb, n0, w.R)
 
     def same_state(n, label):
@@ -169,7 +178,7 @@ def test_brute_force_matches_oracle(orc):
         kn, vn = synth.gen_new_token(w, t)
         nb_new = body(n + 1)
         if nb_new > nb:
-            encode(Kin, Vin, Khat, Vhat, A, nb, nb_new, w.R)
+            encode(Kin, Vin, Khat, Vhat, A, nb, nb_new, w.R, rbits, full)
             nb = nb_new
         for r in range(w.R):
             Kin[r][n], Vin[r][n] = widen(kn[r][0, 0]), widen(vn[r][0, 0])
