@@ -70,6 +70,9 @@ def parse():
                     help="only run a plain elementwise copy of 1 GiB (reference for the byte counters)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write a per-kernel table of the rocprofv3 kernel trace under DIR to --out")
+    ap.add_argument("--summarize-inflight", nargs=2, metavar=("KEY", "DIR"),
+                    help="from a rocprofv3 --pmc TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_sum GRBM_GUI_ACTIVE run of "
+                         "--profile KEY: write the mean reads in flight and their latency to --out")
     ap.add_argument("--summarize-traffic", nargs=5, metavar=("KEY", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of --profile KEY and of "
                          "--copy-calibration): write the calibrated HBM bytes of that kernel family to --out")
@@ -959,6 +962,37 @@ def summarize_traffic(args):
     print("\n".join(lines))
 
 
+def summarize_inflight(args):
+    """Reads in flight and their latency for the main kernel of a family, from one
+    `rocprofv3 --pmc TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_sum GRBM_GUI_ACTIVE` run of
+    `--profile <key>`: LEVEL accumulates the outstanding 128-byte reads every cycle, so
+    LEVEL / active cycles is the mean number in flight and LEVEL / requests their mean
+    latency in cycles."""
+    key, d = args.summarize_inflight
+    fname, kernels, srcs = TRAFFIC[key]
+    main_k = kernels[0]
+    con = _rocprof_db(d)
+    per = {}
+    for name, did, cn, cv in con.execute("select name, dispatch_id, counter_name, counter_value from pmc_events"):
+        if main_k in name:
+            per.setdefault(int(did), {}).setdefault(cn, []).append(float(cv))
+    dids = sorted(per)[-profiled_dispatches(key):]
+    lvl = [sum(per[i]["TCC_EA0_RDREQ_LEVEL_sum"]) for i in dids]
+    req = [sum(per[i]["TCC_EA0_RDREQ_sum"]) for i in dids]
+    act = [max(per[i]["GRBM_GUI_ACTIVE"]) for i in dids]   # the slowest XCD: the dispatch's span
+    mean = lambda v: sum(v) / len(v)
+    inflight = mean([a / b for a, b in zip(lvl, act)])
+    latency = mean([a / b for a, b in zip(lvl, req)])
+    lines = [f"# Reads in flight of {main_k} ({key}) at 32K context (16 heads x 128)",
+             f"command: {args.cmd}", "",
+             "| dispatches | 128-B read requests / dispatch | active cycles / dispatch | reads in flight (mean) | "
+             "read latency (cycles, mean) |", "|---|---|---|---|---|",
+             f"| {len(dids)} | {mean(req):.0f} | {mean(act):.0f} | {inflight:.0f} | {latency:.0f} |", "",
+             f"kernel_source_hash: {source_hash(srcs)}"]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # --------------------------------------------------------------------------- main ----
 def main():
     args = parse()
@@ -966,6 +1000,8 @@ def main():
         return summarize_trace(args)
     if args.summarize_traffic:
         return summarize_traffic(args)
+    if args.summarize_inflight:
+        return summarize_inflight(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "

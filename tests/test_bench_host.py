@@ -58,3 +58,33 @@ def test_counter_mean_takes_the_profiled_dispatches(tmp_path):
     assert bench._counter_per_dispatch(str(tmp_path), "FETCH_SIZE", ("dense_split_kernel",),
                                        bench.profiled_dispatches("dense1"))["dense_split_kernel"] == (500.0, 24)
     assert bench.profiled_dispatches("select") == 3
+
+
+def test_inflight_summary_from_counters(tmp_path):
+    # LEVEL / active cycles = reads in flight, LEVEL / requests = latency; counters summed over
+    # their instances per dispatch, the active cycles taken from the slowest XCD; only the
+    # profiled dispatches (after a warm-up step) count
+    import sqlite3
+    import types
+
+    import bench
+    db = sqlite3.connect(str(tmp_path / "run_results.db"))
+    db.execute("create table pmc_events (name text, dispatch_id integer, counter_name text, counter_value real)")
+    k = "void qkv::sparse_chunk_kernel<128, 4, false, false, 3>"
+    rows = []
+    n = bench.profiled_dispatches("sparse3")
+    for i in range(8 + n):
+        warm = i < 8
+        for inst in range(2):
+            rows.append((k, i, "TCC_EA0_RDREQ_LEVEL_sum", 1.0 if warm else 3.0e6))
+            rows.append((k, i, "TCC_EA0_RDREQ_sum", 1.0 if warm else 1.0e3))
+        for x in range(8):
+            rows.append((k, i, "GRBM_GUI_ACTIVE", 5.0 if warm else (1.0e3 if x == 3 else 10.0)))
+    db.executemany("insert into pmc_events values (?, ?, ?, ?)", rows)
+    db.commit()
+    db.close()
+    out = tmp_path / "s.txt"
+    bench.summarize_inflight(types.SimpleNamespace(summarize_inflight=("sparse3", str(tmp_path)), out=str(out), cmd="c"))
+    row = [l for l in out.read_text().splitlines() if l.startswith(f"| {n} |")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells == [str(n), "2000", "1000", "6000", "3000"]
