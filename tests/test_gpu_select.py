@@ -154,3 +154,21 @@ def test_nonnegative_wide_rows(n):
     for k in (1, -(-n // 10), n // 4, n // 4 + 1, n // 2, n - 1):
         say(f"  select non-negative wide rows n={n} k={k}")
         run_case(S, lse, k)
+
+
+@pytest.mark.parametrize("n", [10240, 10241, 20480, 20481])
+def test_register_row_boundaries(n):
+    # row lengths at the edges of the 10, 20 and 40 scores-per-thread forms, with spread,
+    # tied, non-negative heavy-tailed and partly masked rows
+    g = np.random.default_rng(n + 71)
+    S = np.zeros((1, 4, n), np.float32)
+    S[0, 0] = (g.standard_normal(n) * 1.7).astype(np.float32)
+    S[0, 1] = (g.integers(-6, 7, n) * 0.5).astype(np.float32)
+    S[0, 2] = np.exp(2.0 * g.standard_normal(n)).astype(np.float32)
+    S[0, 3] = g.standard_normal(n).astype(np.float32)
+    S[0, 3, ::3] = -np.inf
+    mx = S.max(-1, keepdims=True).astype(np.float64)
+    lse = (np.log(np.exp(S.astype(np.float64) - mx).sum(-1)) + mx[..., 0]).astype(np.float32)
+    for k in (1, -(-n // 10), n // 3, n - 1):
+        say(f"  select row boundaries n={n} k={k}")
+        run_case(S, lse, k)
