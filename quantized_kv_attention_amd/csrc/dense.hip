@@ -188,6 +188,11 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
     for (int k = 0; k < 32; ++k) acc[k] = 0.f;
     float vb = 0.f;
     float mx, lsum;
+    // Every plane of the chain prepared (loops 1 and 2 of the residual codec): each wave reads
+    // only the logits of its own blocks and tail rows, so it keeps a softmax of its own
+    // (max, sum) and the waves are merged once at the end, with no workgroup barrier between
+    // the key and the value pass.
+    const bool wl = loop == NPRE;
 
     {
         {
@@ -238,7 +243,8 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
                 }
             }
         }
-        __syncthreads();
+        if (wl) wave_sync_lds();  // a wave folds the blocks it reads
+        else __syncthreads();
 
         // K pass, prepared planes: logits of every row of the block summed over the planes.
         // Each block step sets the wave's issue priority from the share of its blocks still
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
                 if (prt == 0) logit[bb * 64 + rsub + RPI * it] = v + bias;
             }
         }
-        __syncthreads();
+        if (!wl) __syncthreads();
         // K pass, remaining planes (sparse planes, or dense planes beyond the prepared ones),
         // in ascending order: their partial logits add up (or, full-state, overwrite)
         for (int p = npre; p < loop; ++p) {
@@ -327,8 +333,9 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
                 v = group_sum<LPR>(v);
                 if (prt == 0 && i < T) logit[L + i] = v;
             }
-            __syncthreads();
+            if (!wl) __syncthreads();
         }
+        if (wl) wave_sync_lds();
         // The first block's value codes are in flight during the softmax.
         uint4 wv[NPRE][NLD];
         float2 mv[NPRE][NLD];
@@ -351,19 +358,57 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
             }
         };
         load_v(blkP);
-        float lm = -__builtin_huge_valf();
-        for (int i = tid; i < L + T; i += 256) {
-            if (srow) srow[j0 + i] = logit[i];  // the tail rows follow the split's body rows (j0 + L == n_body)
-            lm = fmaxf(lm, logit[i]);
+        if (wl) {
+            // this wave's rows: lane l of each of its blocks, then its tail rows (RPI-row
+            // groups wave, wave + 4, ... as the tail passes take them)
+            float lm = -__builtin_huge_valf();
+            for (int bb = wave; bb < nb; bb += 4) {
+                const float x = logit[bb * 64 + lane];
+                if (srow) srow[j0 + bb * 64 + lane] = x;
+                lm = fmaxf(lm, x);
+            }
+            for (int i0 = wave * RPI; i0 < T; i0 += 4 * RPI) {
+                const int i = i0 + lane;
+                if (lane < RPI && i < T) {
+                    const float x = logit[L + i];
+                    if (srow) srow[j0 + L + i] = x;  // j0 + L == n_body
+                    lm = fmaxf(lm, x);
+                }
+            }
+            mx = wave_max(lm);
+            float ls = 0.f;
+            if (mx != -__builtin_huge_valf()) {
+                for (int bb = wave; bb < nb; bb += 4) {
+                    const float pv = __expf(logit[bb * 64 + lane] - mx);
+                    logit[bb * 64 + lane] = pv;
+                    ls += pv;
+                }
+                for (int i0 = wave * RPI; i0 < T; i0 += 4 * RPI) {
+                    const int i = i0 + lane;
+                    if (lane < RPI && i < T) {
+                        const float pv = __expf(logit[L + i] - mx);
+                        logit[L + i] = pv;
+                        ls += pv;
+                    }
+                }
+            }
+            lsum = wave_sum(ls);
+            wave_sync_lds();
+        } else {
+            float lm = -__builtin_huge_valf();
+            for (int i = tid; i < L + T; i += 256) {
+                if (srow) srow[j0 + i] = logit[i];  // the tail rows follow the split's body rows (j0 + L == n_body)
+                lm = fmaxf(lm, logit[i]);
+            }
+            mx = block_reduce_max(lm, red);
+            float ls = 0.f;
+            for (int i = tid; i < L + T; i += 256) {
+                const float pv = __expf(logit[i] - mx);
+                logit[i] = pv;
+                ls += pv;
+            }
+            lsum = block_reduce_sum(ls, red);
         }
-        mx = block_reduce_max(lm, red);
-        float ls = 0.f;
-        for (int i = tid; i < L + T; i += 256) {
-            const float pv = __expf(logit[i] - mx);
-            logit[i] = pv;
-            ls += pv;
-        }
-        lsum = block_reduce_sum(ls, red);
 
         // V pass, remaining planes.  Residual codec: every plane adds its part of each stored
         // position's value.  Full-state codec: the deepest plane storing a position takes its
@@ -485,6 +530,26 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
     if (rsub == 0) {
 #pragma unroll
         for (int k = 0; k < 32; ++k) ored[wave][32 * prt + k] = acc[k] + vb;
+    }
+    if (wl) {
+        // the waves' (max, sum, o) merged on the workgroup maximum, in wave order
+        __shared__ float wmx[4], wls[4];
+        if (lane == 0) {
+            wmx[wave] = mx;
+            wls[wave] = lsum;
+        }
+        __syncthreads();
+        const float M = fmaxf(fmaxf(wmx[0], wmx[1]), fmaxf(wmx[2], wmx[3]));
+        float e[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) e[w] = wmx[w] == -__builtin_huge_valf() ? 0.f : __expf(wmx[w] - M);
+        for (int c = tid; c < D; c += 256)
+            out[2 + c] = fmaf(ored[0][c], e[0], ored[1][c] * e[1]) + fmaf(ored[2][c], e[2], ored[3][c] * e[3]);
+        if (tid == 0) {
+            out[0] = M;
+            out[1] = fmaf(wls[0], e[0], wls[1] * e[1]) + fmaf(wls[2], e[2], wls[3] * e[3]);
+        }
+        return;
     }
     __syncthreads();
     for (int c = tid; c < D; c += 256) out[2 + c] = (ored[0][c] + ored[1][c]) + (ored[2][c] + ored[3][c]);
