@@ -97,6 +97,7 @@ __device__ __forceinline__ float dpp(float v) {
 }
 constexpr int kQuadXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kQuadEven = 0xA0;         // quad_perm [0,0,2,2]: lanes 1 and 3 of a quad read lanes 0 and 2
 constexpr int kRowRor4 = 0x124;         // row_ror:4
 constexpr int kRowRor8 = 0x128;         // row_ror:8 (lane i of a 16-lane row reads lane i ^ 8)
 constexpr int kRowMirror = 0x140;       // row_mirror: lane i of a 16-lane row reads lane 15 - i

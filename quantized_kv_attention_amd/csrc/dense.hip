@@ -345,14 +345,17 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
 #pragma unroll
                 for (int it = 0; it < NLD; ++it) {
                     const int row = rsub + RPI * it;
+                    // a row's value meta: the even lanes of its quad load it (lane 2 the second
+                    // 64-channel group at d = 128), the odd lanes take it by DPP at use
+                    mv[p][it] = make_float2(0.f, 0.f);
                     if (p == 0 || RBITS == 4) {
                         const uint8_t* bp = block_ptr<D, 4>(ca.p[p], ca.H, b, h, blk);
                         wv[p][it] = ld_codes32<4>(bp + Block<D, 4>::vc(row) + prt * Block<D, 4>::kLaneBytes);
-                        mv[p][it] = ld_stream_f2(bp + Block<D, 4>::vm(row) + (prt >> 1) * 8);
+                        if ((prt & 1) == 0) mv[p][it] = ld_stream_f2(bp + Block<D, 4>::vm(row) + (prt >> 1) * 8);
                     } else {
                         const uint8_t* bp = block_ptr<D, RBITS>(ca.p[p], ca.H, b, h, blk);
                         wv[p][it] = ld_codes32<RBITS>(bp + Block<D, RBITS>::vc(row) + prt * Block<D, RBITS>::kLaneBytes);
-                        mv[p][it] = ld_stream_f2(bp + Block<D, RBITS>::vm(row) + (prt >> 1) * 8);
+                        if ((prt & 1) == 0) mv[p][it] = ld_stream_f2(bp + Block<D, RBITS>::vm(row) + (prt >> 1) * 8);
                     }
                 }
             }
@@ -465,11 +468,12 @@ __global__ __launch_bounds__(256, 3) void dense_split_kernel(CacheArg ca, int lo
                 const float pw = logit[bb * 64 + rsub + RPI * it];
 #pragma unroll
                 for (int p = 0; p < NPRE; ++p) {
-                    vb = fmaf(pw, mv[p][it].y, vb);
+                    const float vs = dpp<kQuadEven>(mv[p][it].x), vz = dpp<kQuadEven>(mv[p][it].y);
+                    vb = fmaf(pw, vz, vb);
                     if (p == 0 || RBITS == 4)
-                        axpy32_bits<4>(wv[p][it], pw * mv[p][it].x * kFp8CodeScale, acc);
+                        axpy32_bits<4>(wv[p][it], pw * vs * kFp8CodeScale, acc);
                     else
-                        axpy32_bits<RBITS>(wv[p][it], pw * mv[p][it].x * kFp8CodeScale, acc);
+                        axpy32_bits<RBITS>(wv[p][it], pw * vs * kFp8CodeScale, acc);
                 }
             }
         }
