@@ -227,6 +227,71 @@ __global__ __launch_bounds__(64 * kSpWaves, 1) void sparse_chunk_kernel(CacheArg
             bf16x8(*reinterpret_cast<const uint4*>(ca.tail_k[loop - 1] + off), kh);
             bf16x8(*reinterpret_cast<const uint4*>(ca.tail_v[loop - 1] + off), vc);
             bf16x8(*reinterpret_cast<const uint4*>(ca.tail_v[loop - 2] + off), vh);
+        } else if constexpr (ROUNDS == kWaveRoundsSmall) {
+            // Launches too small to fill the chip wait on memory latency, not on bandwidth:
+            // every load that depends on no other plane's is issued together (the sparse
+            // planes' slot lookups with the dense planes' data), so a round waits on three
+            // memory round trips (its entry, those, then the sparse planes' data) instead of
+            // one or two per plane.  Registers are not short at this wave count.
+            constexpr int NPM = 4;  // this kernel's chains have at most four planes
+            int sl[NPM];
+#pragma unroll
+            for (int p = 0; p < NPM; ++p) {
+                const PlaneArg& P = ca.p[p < loop ? p : 0];
+                sl[p] = p >= loop ? -1 : (P.dense ? j : P.rowmap[(size_t)b * cap + j]);
+            }
+            SlotData sd[NPM];
+            bool ok[NPM];
+#pragma unroll
+            for (int p = 0; p < NPM; ++p) {
+                const PlaneArg& P = ca.p[p < loop ? p : 0];
+                ok[p] = sl[p] >= 0 && sl[p] < P.n_blocks * 64;
+                const int slot = ok[p] ? sl[p] : 0;  // a plane not read loads a valid slot
+                if (p == 0 || RBITS == 4)
+                    sd[p] = load_slot<D, 4>(P, ca.H, b, h, slot, prt, c0);
+                else
+                    sd[p] = load_slot<D, RBITS>(P, ca.H, b, h, slot, prt, c0);
+            }
+            bool act_r = false;
+#pragma unroll
+            for (int p = 0; p < NPM; ++p) {
+                if (!ok[p]) continue;
+                float code[8], vcode[8];
+                if (p == 0 || RBITS == 4) {
+                    codes8_bits<4>(sd[p].kw, code);
+                    codes8_bits<4>(sd[p].vw, vcode);
+                } else {
+                    codes8_bits<RBITS>(sd[p].kw, code);
+                    codes8_bits<RBITS>(sd[p].vw, vcode);
+                }
+                const float ks[8] = {sd[p].s0.x, sd[p].s0.y, sd[p].s0.z, sd[p].s0.w,
+                                     sd[p].s1.x, sd[p].s1.y, sd[p].s1.z, sd[p].s1.w};
+                const float kz[8] = {sd[p].z0.x, sd[p].z0.y, sd[p].z0.z, sd[p].z0.w,
+                                     sd[p].z1.x, sd[p].z1.y, sd[p].z1.z, sd[p].z1.w};
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const float deq = fmaf(code[c], ks[c], kz[c]);
+                    kh[c] = (p == 0 || REPLACE) ? deq : kh[c] + deq;
+                }
+                if (p < loop - 1) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        const float deq = fmaf(vcode[c], sd[p].vm.x, sd[p].vm.y);
+                        vh[c] = (p == 0 || REPLACE) ? deq : vh[c] + deq;
+                    }
+                } else {
+                    act_r = true;
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        const float deq = fmaf(vcode[c], sd[p].vm.x, sd[p].vm.y);
+                        vc[c] = REPLACE ? deq : vh[c] + deq;
+                    }
+                }
+            }
+            if (!act_r) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) vc[c] = vh[c];
+            }
         } else {
             bool act_r = false;
             // one plane at a time: its slot, then its data
