@@ -122,16 +122,20 @@ def workspace_bytes(batch, heads, head_dim, max_ctx, max_k) -> int:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """A tensor's device address, or an address given as an int, or None (a NULL argument);
+    the entry points' argtypes turn ints into pointers."""
+    if t is None or isinstance(t, int):
+        return t
+    return t.data_ptr()
 
 
 def _stream(stream):
     if stream is None:
         import torch
-        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, int):
-        return ctypes.c_void_p(stream)
-    return ctypes.c_void_p(stream.cuda_stream)
+        return stream
+    return stream.cuda_stream
 
 
 def _check(fn, st):

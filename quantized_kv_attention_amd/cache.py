@@ -255,6 +255,22 @@ class DecodeBuffers:
             self.idx, self.p_sel, self.mass, self.ws = stack.idx, stack.p_sel, stack.mass, stack.ws
             self.layer = layer
 
+    def out_ptrs(self, loop: int):
+        """Device addresses of o[loop - 1] and o_f32[loop - 1], taken from the current tensors
+        at each call (no views built; the attributes may be replaced)."""
+        r = loop - 1
+        return (self.o.data_ptr() + r * self.o.stride(0) * self.o.element_size(),
+                self.o_f32.data_ptr() + r * self.o_f32.stride(0) * self.o_f32.element_size())
+
+    def selection_ptrs(self, loop: int, k: int):
+        """Device addresses of the (idx, p_sel, mass) that selection(loop, k) views, taken from
+        the current tensors at each call."""
+        r = loop - 1
+        off = self.layer * self.B * self.H * max(k, 1)
+        return (self.idx.data_ptr() + 4 * (r * self.idx.stride(0) + off),
+                self.p_sel.data_ptr() + 4 * (r * self.p_sel.stride(0) + off),
+                self.mass.data_ptr() + 4 * (r * self.mass.stride(0) + self.layer * self.B * self.mass.stride(1)))
+
     def selection(self, loop: int, k: int):
         """Views (idx, p_sel, mass) of loop `loop`'s selection of k columns."""
         r = loop - 1
@@ -316,16 +332,19 @@ def decode_loop(cache: LayerCache, bufs: DecodeBuffers, loop: int, q, n_dense: i
     flush: this loop's QkvFlush (LayerCache.flush_args), encoded by the same call."""
     r = loop - 1
     main = torch.cuda.current_stream() if stream is None else stream
+    o, o32 = bufs.out_ptrs(loop)
     if loop <= n_dense:
-        attn_decode_dense(cache, loop, q, sm, bufs.o[r], bufs.o_f32[r], bufs.scores if need_scores else None,
+        attn_decode_dense(cache, loop, q, sm, o, o32, bufs.scores if need_scores else None,
                           bufs.lse, bufs.ws, main, k_new=k_new, v_new=v_new, flush=flush)
     else:
         assert k <= bufs.max_k
-        idx, ps, mass = bufs.selection(loop, k)
         if not selected:
+            idx, ps, mass = bufs.selection(loop, k)
             select_columns(bufs.scores, bufs.lse, cache.n_ctx, k, idx, ps, mass, None, main)
-        attn_decode_sparse(cache, loop, q, sm, idx, ps, mass, k, bufs.o_f32[r - 1], bufs.lse,
-                           bufs.scores if need_scores else None, bufs.o[r], bufs.o_f32[r], bufs.ws, main,
+        idx, ps, mass = bufs.selection_ptrs(loop, k)
+        o32_prev = bufs.out_ptrs(loop - 1)[1]
+        attn_decode_sparse(cache, loop, q, sm, idx, ps, mass, k, o32_prev, bufs.lse,
+                           bufs.scores if need_scores else None, o, o32, bufs.ws, main,
                            k_new=k_new, v_new=v_new, flush=flush)
 
 
