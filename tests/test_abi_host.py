@@ -198,3 +198,27 @@ def test_layer_stack_layout_cpu():
     whole = st.idx[2, :6 * 3 * k].view(6, 3, k)
     for l, b in enumerate(st.layers):
         assert torch.equal(b.selection(3, k)[0], whole[2 * l:2 * l + 2])
+
+
+def test_call_addresses_follow_the_current_tensors_cpu():
+    # the decode calls pass addresses as integers (DecodeBuffers.out_ptrs / selection_ptrs):
+    # they must equal those of the views they stand for, for a standalone layer and for every
+    # layer of a stack, and follow a tensor that replaced an attribute (an address kept from
+    # the replaced tensor would point at freed memory)
+    import torch
+    from quantized_kv_attention_amd import cache as qcache
+    c = qcache.LayerCache(2, 3, 128, 4, 512, device="cpu")
+    cs = [qcache.LayerCache(2, 3, 128, 4, 512, device="cpu") for _ in range(3)]
+    st = qcache.LayerStack(cs, max_k=40, device="cpu")
+    for b in [qcache.DecodeBuffers(c, max_k=50, device="cpu")] + st.layers:
+        for loop in range(1, 5):
+            o, o32 = b.out_ptrs(loop)
+            assert (o, o32) == (b.o[loop - 1].data_ptr(), b.o_f32[loop - 1].data_ptr())
+        for loop in (3, 4):
+            for k in (0, 1, 17, 40):
+                assert b.selection_ptrs(loop, k) == tuple(t.data_ptr() for t in b.selection(loop, k))
+    b = st.layers[1]
+    b.o_f32 = torch.zeros_like(b.o_f32)
+    b.idx = torch.zeros_like(b.idx)
+    assert b.out_ptrs(2)[1] == b.o_f32[1].data_ptr()
+    assert b.selection_ptrs(3, 17)[0] == b.selection(3, 17)[0].data_ptr()
